@@ -1,0 +1,155 @@
+"""Planted mistakes in the oracle (CPU only): each must make one of the named
+pins fail, which shows the pins can see that kind of mistake."""
+
+import numpy as np
+import pytest
+
+import oracle.post as O
+import pins
+
+_orig = {n: getattr(O, n) for n in dir(O) if callable(getattr(O, n))}
+
+
+def _sanitize_no_posinf(lse):
+    v = np.asarray(lse, dtype=np.float64).copy()
+    v[np.isnan(v)] = -np.inf
+    return v
+
+
+def _sanitize_no_nan(lse):
+    v = np.asarray(lse, dtype=np.float64).copy()
+    v[v == np.inf] = -np.inf
+    return v
+
+
+def _weights_no_m_reset(lse):
+    lse = np.asarray(lse, dtype=np.float64)
+    m = lse.max(axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        e = np.exp(lse - m)
+    tot = e.sum(axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w = np.where(e == 0.0, 0.0, e / tot)
+    return w, e
+
+
+def _weights_exp2(lse):
+    lse = np.asarray(lse, dtype=np.float64)
+    m = lse.max(axis=-1, keepdims=True)
+    m = np.where(m == -np.inf, 0.0, m)
+    e = np.exp2(lse - m)
+    tot = e.sum(axis=-1, keepdims=True)
+    safe = np.where(tot == 0.0, 1.0, tot)
+    return np.where((tot == 0.0) | (e == 0.0), 0.0, e / safe), e
+
+
+def _weights_unnormalised(lse):
+    lse = np.asarray(lse, dtype=np.float64)
+    m = lse.max(axis=-1, keepdims=True)
+    m = np.where(m == -np.inf, 0.0, m)
+    e = np.exp(lse - m)
+    return e, e
+
+
+def _merge_values_no_mask(o, lse):
+    o = np.asarray(o, dtype=np.float64)
+    w, _ = O.merge_weights(np.moveaxis(O.sanitize_lse(lse), 0, -1))
+    w = np.moveaxis(w, -1, 0)[..., None]
+    with np.errstate(invalid="ignore"):
+        return (w * o).sum(axis=0), (w * np.abs(o)).sum(axis=0)
+
+
+def _rne_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _rne_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(x).astype(np.uint16) << 15
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    q = np.maximum(e - 8, -133)
+    s = np.ldexp(a, -q)
+    r = np.floor(s + 0.5)
+    with np.errstate(over="ignore"):
+        f32 = np.ldexp(r, q).astype(np.float32)
+    return ((f32.view(np.uint32) >> 16).astype(np.uint16)) | sign
+
+
+def _e8m0_floor(block_bits):
+    mag = (np.asarray(block_bits, dtype=np.uint16) & 0x7FFF).astype(np.int64)
+    return np.maximum((mag.max(axis=-1) >> 7) - 2, 1)
+
+
+def _e8m0_no_clamp(block_bits):
+    mag = (np.asarray(block_bits, dtype=np.uint16) & 0x7FFF).astype(np.int64)
+    return np.maximum(((mag.max(axis=-1) + 0x20) >> 7) - 2, 0)
+
+
+def _e2m1_ties_away(y):
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), 8.0)
+    d = np.abs(a[..., None] - O.E2M1_MAG)
+    best = d.min(axis=-1, keepdims=True)
+    hit = d == best
+    idx = 7 - np.argmax(hit[..., ::-1], axis=-1)  # the larger candidate
+    return (idx | (np.signbit(y).astype(np.int64) << 3)).astype(np.uint8)
+
+
+def _e2m1_plus_zero(y):
+    n = _orig["e2m1_nibble"](y)
+    return np.where((n & 7) == 0, 0, n).astype(np.uint8)
+
+
+def _quant_swapped_nibbles(bits):
+    c, s = _orig["quantize_mxfp4"](bits)
+    return ((c >> 4) | (c << 4)).astype(np.uint8), s
+
+
+def _wuv_bias_off(lc, ls, wc, ws):
+    return _orig["wuv_exact"](lc, ls, wc, np.minimum(np.asarray(ws, np.int64) + 1, 254).astype(np.uint8))
+
+
+def _wuv_rows_reversed(lc, ls, wc, ws):
+    return _orig["wuv_exact"](lc, ls, wc[:, ::-1], ws[:, ::-1])
+
+
+def _gate_transposed(acc_bf, gate_bits):
+    T = acc_bf.shape[0]
+    a = O.bf16_to_f64(acc_bf).transpose(0, 2, 1).reshape(T, O.NH * O.VD)
+    return O.rne_bf16(a * O.bf16_to_f64(gate_bits).reshape(T, -1))
+
+
+MUTATIONS = [
+    ("sanitize misses +inf", "sanitize_lse", _sanitize_no_posinf, [pins.pin_nan_inf_as_neg_inf]),
+    ("sanitize misses NaN", "sanitize_lse", _sanitize_no_nan, [pins.pin_nan_inf_as_neg_inf]),
+    ("max not reset when all empty", "merge_weights", _weights_no_m_reset, [pins.pin_all_empty_zero]),
+    ("base-2 LSEs", "merge_weights", _weights_exp2, [pins.pin_textbook_attention]),
+    ("weights not normalised", "merge_weights", _weights_unnormalised, [pins.pin_textbook_attention]),
+    ("dead rows not masked", "merge_values", _merge_values_no_mask, [pins.pin_dead_rows_ignored]),
+    ("bf16 by truncation", "rne_bf16", _rne_truncate, [pins.pin_rne_bf16_vs_torch]),
+    ("bf16 ties away", "rne_bf16", _rne_ties_away, [pins.pin_rne_bf16_vs_torch]),
+    ("floor scale rule", "e8m0_even", _e8m0_floor, [pins.pin_scale_rule_closed_form, pins.pin_quant_golden]),
+    ("scale not raised to 1", "e8m0_even", _e8m0_no_clamp, [pins.pin_quant_golden]),
+    ("E2M1 ties away", "e2m1_nibble", _e2m1_ties_away, [pins.pin_quant_golden]),
+    ("E2M1 loses -0", "e2m1_nibble", _e2m1_plus_zero, [pins.pin_quant_golden]),
+    ("nibble order swapped", "quantize_mxfp4", _quant_swapped_nibbles, [pins.pin_quant_golden]),
+    ("scale bias off by one", "wuv_exact", _wuv_bias_off, [pins.pin_wuv_one_hot]),
+    ("W_V rows reversed", "wuv_exact", _wuv_rows_reversed, [pins.pin_wuv_one_hot]),
+    ("gate columns transposed", "gate_core", _gate_transposed, [pins.pin_gate_core]),
+]
+
+
+@pytest.mark.parametrize("name,attr,fn,catchers", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, attr, fn, catchers):
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in catchers:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake '{name}' passed every pin in {[p.__name__ for p in catchers]}"
