@@ -1,0 +1,136 @@
+/*
+ * mla_post: MLA decode post-attention on AMD MI355X (gfx950).
+ *
+ * The operation is the one the vLLM API-docs page for module
+ * vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_back
+ * describes (module docstring; functions mla_post, host_args,
+ * stage_combine, combine_splits, combine_ranks, sane, stage_uv, wv_loads).
+ * For every token t < S and head h < 12:
+ *
+ *   1. merge the n bf16 partial rows o[j, t, h, 0:512] with their float32
+ *      natural-log LSEs (NaN and +inf count as -inf; m = max LSE, 0 when all
+ *      are -inf; w_j = exp(lse_j - m) / sum exp; a row of weight 0 is not
+ *      read and contributes nothing). With n == 1 and lse == NULL the row is
+ *      the final attention output and is used as is;
+ *   2. round the float32 sum to bf16 latents (round to nearest even);
+ *   3. quantise each block of 32 latents to MXFP4: E8M0 scale code
+ *      c = max(1, Eb(amax) + [mantissa fraction of amax >= 0.75] - 2), amax
+ *      the largest bf16 magnitude in the block; E2M1 elements of x / 2^(c-127)
+ *      rounded to nearest, ties to the even code, saturating at 6, sign kept;
+ *   4. multiply by the head's MXFP4 W_V[h] (128 x 512) with scaled FP4 MFMA
+ *      (float32 accumulation);
+ *   5. core[t, 128 h + v] = bf16( bf16(acc[v]) * gate[t, 128 h + v] ).
+ *
+ * All entry points are host functions with C linkage. Device pointers are
+ * caller-owned device memory; the library keeps no pointer after a call
+ * returns, allocates nothing per call and holds no mutable global state, so
+ * calls are thread-safe. Work is enqueued asynchronously on the caller's HIP
+ * stream. Validation failures are reported synchronously, launch nothing and
+ * leave every output untouched.
+ */
+#ifndef MLA_POST_H
+#define MLA_POST_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_POST_VERSION 1
+
+/* Fixed shapes (the page's per-rank Kimi-K3 shapes at 8-way tensor parallelism). */
+#define MLA_POST_HEADS 12   /* local heads */
+#define MLA_POST_KVL 512    /* latent width */
+#define MLA_POST_VD 128     /* W_V rows (value width) per head */
+#define MLA_POST_GROWS 1536 /* gate / core row length = 12 * 128 */
+#define MLA_POST_NMAX 512   /* largest number of partials per (token, head) */
+
+/* Status codes (0 = success, negative = error). */
+#define MLA_POST_OK 0
+#define MLA_POST_EINVAL (-1)       /* null pointer, bad size, lse NULL with n > 1 */
+#define MLA_POST_ESTRIDE (-2)      /* a stride that is negative or not a multiple the loads need */
+#define MLA_POST_EALIGN (-3)       /* a pointer not aligned as its loads or stores need */
+#define MLA_POST_ERANGE (-4)       /* an offset that overflows 64-bit arithmetic */
+#define MLA_POST_EUNSUPPORTED (-5) /* n > MLA_POST_NMAX, or cols not a multiple of 32 */
+#define MLA_POST_ELAUNCH (-6)      /* the HIP runtime refused the launch (message: mla_post_last_hip_error) */
+
+/*
+ * Arguments of one mla_post call. Strides of o and lse are in elements; those
+ * of w_v and w_v_scale are in bytes. The partial row j of (t, h) is the 512
+ * contiguous bf16 at o + j*o_sj + t*o_st + h*o_sh (the innermost stride is 1,
+ * as the page's host_args asserts). One layout covers the three cases the page
+ * names:
+ *   - split-KV partials, dense [n, S, 12, 512]: (o_sj, o_st, o_sh) = (S*6144, 6144, 512);
+ *   - decode-context-parallel partials gathered on one GPU, o [S, >= n*12, 512]
+ *     with rank r's partial of local head h at gathered head r*12 + h:
+ *     (o_sj, o_st, o_sh) = (12*512, head_rows*512, 512);
+ *   - one partial, no LSE (n == 1, lse == NULL): o [S, 12, 512].
+ */
+typedef struct mla_post_args {
+  uint32_t struct_size; /* sizeof(mla_post_args) */
+  int32_t n;            /* partials per (token, head): splits or ranks, 1..MLA_POST_NMAX */
+  int32_t S;            /* tokens; 0 is a no-op */
+  int32_t reserved;
+
+  const void* o;            /* bf16 partials, device, 16-byte aligned */
+  int64_t o_sj, o_st, o_sh; /* >= 0, multiples of 8 elements */
+
+  const float* lse;         /* float32 LSEs, device, or NULL only when n == 1 */
+  int64_t l_sj, l_st, l_sh; /* >= 0 */
+
+  const uint8_t* w_v;  /* MXFP4 W_V codes, logical (12, 128, 256) bytes: byte of
+                          (h, v, k) at w_v + h*w_sh + v*w_sv + k/2, element 2i
+                          in the low nibble of byte i; 16-byte aligned */
+  int64_t w_sh, w_sv;  /* bytes, >= 0, multiples of 16 */
+
+  const uint8_t* w_v_scale;  /* E8M0 scales, logical (12, 128, 16): byte of
+                                (h, v, b) at + h*s_sh + v*s_sv + b*s_sb */
+  int64_t s_sh, s_sv, s_sb;  /* bytes, >= 0 */
+
+  const void* gate; /* bf16 [S, 1536] dense, 8-byte aligned */
+  void* core;       /* bf16 [S, 1536] dense, 8-byte aligned; every row t < S is
+                       written, nothing else is */
+
+  /* Optional stage outputs (NULL to skip), written by the same kernel with
+   * the same arithmetic: latents bf16 [S, 12, 512] (16-byte aligned), MXFP4
+   * latent codes u8 [S, 12, 256] (4-byte aligned), E8M0 latent scale codes
+   * u8 [S, 12, 16]. */
+  void* dbg_lat;
+  void* dbg_codes;
+  void* dbg_scales;
+} mla_post_args;
+
+/* Validate and enqueue one mla_post call on `stream` (a hipStream_t; NULL is
+ * the default stream). Returns MLA_POST_OK or a negative status. */
+int mla_post(const mla_post_args* a, void* stream);
+
+/* The validation of mla_post alone: host only, touches no device memory and
+ * needs no GPU. Returns what mla_post would return before launching. */
+int mla_post_check(const mla_post_args* a);
+
+/*
+ * Quantise `rows` rows of `cols` bf16 values (cols a multiple of 32, at most
+ * 8192) to MXFP4 with the same rule as step 3 above: row r's values at
+ * x + r*x_stride (elements, 16-byte aligned rows), its codes (cols/2 bytes) to
+ * codes + r*c_stride and its E8M0 scale codes (cols/32 bytes) to
+ * scales + r*s_stride (bytes). This is how W_V is put into MXFP4 from bf16.
+ * Asynchronous on `stream`; same status codes.
+ */
+int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stride, uint8_t* codes,
+                       int64_t c_stride, uint8_t* scales, int64_t s_stride, void* stream);
+
+/* Static description of a status code. */
+const char* mla_post_strerror(int status);
+
+/* The HIP error string of the last MLA_POST_ELAUNCH on this thread, or "". */
+const char* mla_post_last_hip_error(void);
+
+/* MLA_POST_VERSION of the library. */
+int mla_post_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_POST_H */

@@ -1,0 +1,265 @@
+"""mla_split_kv_amd: MLA decode post-attention (LSE merge -> bf16 latents ->
+MXFP4 -> FP4-MFMA W_UV -> gate) on AMD MI355X.
+
+A thin ctypes binding over the C-ABI library ``libmla_post.so`` (declared in
+``include/mla_post.h``): it checks torch tensors' dtypes, shapes and devices,
+marshals pointers and strides, and enqueues the call on torch's current HIP
+stream. Every step of the computation runs in the library's HIP kernels; there
+is no fallback. When the library has not been built, ``load()`` raises.
+
+The operation follows the vLLM API-docs page for module
+``vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_back``
+(functions mla_post and host_args for the interface).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime before the library resolves its own
+
+NH, KVL, VD, GROWS = 12, 512, 128, 1536
+NMAX = 512
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_post.so")
+
+STATUS = {
+    0: "MLA_POST_OK",
+    -1: "MLA_POST_EINVAL",
+    -2: "MLA_POST_ESTRIDE",
+    -3: "MLA_POST_EALIGN",
+    -4: "MLA_POST_ERANGE",
+    -5: "MLA_POST_EUNSUPPORTED",
+    -6: "MLA_POST_ELAUNCH",
+}
+
+
+class MlaPostArgs(ctypes.Structure):
+    """Mirror of ``mla_post_args`` in include/mla_post.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("n", ctypes.c_int32),
+        ("S", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("o", ctypes.c_void_p),
+        ("o_sj", ctypes.c_int64),
+        ("o_st", ctypes.c_int64),
+        ("o_sh", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("l_sj", ctypes.c_int64),
+        ("l_st", ctypes.c_int64),
+        ("l_sh", ctypes.c_int64),
+        ("w_v", ctypes.c_void_p),
+        ("w_sh", ctypes.c_int64),
+        ("w_sv", ctypes.c_int64),
+        ("w_v_scale", ctypes.c_void_p),
+        ("s_sh", ctypes.c_int64),
+        ("s_sv", ctypes.c_int64),
+        ("s_sb", ctypes.c_int64),
+        ("gate", ctypes.c_void_p),
+        ("core", ctypes.c_void_p),
+        ("dbg_lat", ctypes.c_void_p),
+        ("dbg_codes", ctypes.c_void_p),
+        ("dbg_scales", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = (
+    "mla_post",
+    "mla_post_check",
+    "mla_quantize_mxfp4",
+    "mla_post_strerror",
+    "mla_post_last_hip_error",
+    "mla_post_version",
+)
+
+_lib = None
+
+
+class MlaPostError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmla_post.so (raises FileNotFoundError when it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(f"{LIB_PATH} is not built: run `python -m mla_split_kv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.mla_post.argtypes = [ctypes.POINTER(MlaPostArgs), ctypes.c_void_p]
+    lib.mla_post.restype = ctypes.c_int
+    lib.mla_post_check.argtypes = [ctypes.POINTER(MlaPostArgs)]
+    lib.mla_post_check.restype = ctypes.c_int
+    lib.mla_quantize_mxfp4.argtypes = [
+        ctypes.c_void_p,
+        ctypes.c_int64,
+        ctypes.c_int32,
+        ctypes.c_int64,
+        ctypes.c_void_p,
+        ctypes.c_int64,
+        ctypes.c_void_p,
+        ctypes.c_int64,
+        ctypes.c_void_p,
+    ]
+    lib.mla_quantize_mxfp4.restype = ctypes.c_int
+    lib.mla_post_strerror.argtypes = [ctypes.c_int]
+    lib.mla_post_strerror.restype = ctypes.c_char_p
+    lib.mla_post_last_hip_error.argtypes = []
+    lib.mla_post_last_hip_error.restype = ctypes.c_char_p
+    lib.mla_post_version.argtypes = []
+    lib.mla_post_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _raise(lib, st: int):
+    if st != 0:
+        detail = lib.mla_post_strerror(st).decode()
+        if st == -6:
+            detail += ": " + lib.mla_post_last_hip_error().decode()
+        raise MlaPostError(st, detail)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(cond: bool, exc, msg: str):
+    if not cond:
+        raise exc(msg)
+
+
+def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None) -> MlaPostArgs:
+    """Validate tensors (the checks of the page's host_args) and fill the struct.
+
+    o      bf16 [n, S, 12, 512] view, innermost stride 1 (any other strides)
+    lse    float32 [n, S, 12] view, or None when n == 1 (o is then the final
+           attention output)
+    w_v    uint8 [12, 128, 256] MXFP4 codes, innermost stride 1
+    w_v_scale uint8 [12, 128, 16] E8M0 codes, any strides
+    gate, core  bf16 [S, 1536], contiguous
+    dbg    optional (lat bf16 [S,12,512], codes u8 [S,12,256], scales u8 [S,12,16])
+    """
+    _need(o.dim() == 4 and o.shape[2:] == (NH, KVL), ValueError, f"o must be [n, S, 12, 512], got {tuple(o.shape)}")
+    n, S = int(o.shape[0]), int(o.shape[1])
+    _need(o.dtype == torch.bfloat16, TypeError, "o must be bfloat16")
+    _need(o.stride(-1) == 1, ValueError, "o's innermost stride must be 1")
+    if lse is None:
+        _need(n == 1, ValueError, "lse may be omitted only with one partial")
+    else:
+        _need(lse.dtype == torch.float32, TypeError, "lse must be float32")
+        _need(tuple(lse.shape) == (n, S, NH), ValueError, f"lse must be [{n}, {S}, 12], got {tuple(lse.shape)}")
+    _need(w_v.dtype == torch.uint8 and tuple(w_v.shape) == (NH, VD, KVL // 2), TypeError, "w_v must be uint8 [12,128,256]")
+    _need(w_v.stride(-1) == 1, ValueError, "w_v's innermost stride must be 1")
+    _need(
+        w_v_scale.dtype == torch.uint8 and tuple(w_v_scale.shape) == (NH, VD, KVL // 32),
+        TypeError,
+        "w_v_scale must be uint8 [12,128,16]",
+    )
+    for name, t in (("gate", gate), ("core", core)):
+        _need(t.dtype == torch.bfloat16, TypeError, f"{name} must be bfloat16")
+        _need(tuple(t.shape) == (S, GROWS), ValueError, f"{name} must be [{S}, 1536], got {tuple(t.shape)}")
+        _need(t.is_contiguous(), ValueError, f"{name} must be contiguous")
+    dev = core.device
+    tensors = [o, w_v, w_v_scale, gate, core] + ([] if lse is None else [lse])
+    _need(all(t.device == dev for t in tensors), ValueError, "all tensors must be on one device")
+    a = MlaPostArgs()
+    a.struct_size = ctypes.sizeof(MlaPostArgs)
+    a.n, a.S = n, S
+    a.o = o.data_ptr()
+    a.o_sj, a.o_st, a.o_sh = o.stride(0), o.stride(1), o.stride(2)
+    if lse is not None:
+        a.lse = lse.data_ptr()
+        a.l_sj, a.l_st, a.l_sh = lse.stride(0), lse.stride(1), lse.stride(2)
+    a.w_v = w_v.data_ptr()
+    a.w_sh, a.w_sv = w_v.stride(0), w_v.stride(1)
+    a.w_v_scale = w_v_scale.data_ptr()
+    a.s_sh, a.s_sv, a.s_sb = w_v_scale.stride(0), w_v_scale.stride(1), w_v_scale.stride(2)
+    a.gate = gate.data_ptr()
+    a.core = core.data_ptr()
+    if dbg is not None:
+        lat, codes, scales = dbg
+        _need(lat.dtype == torch.bfloat16 and tuple(lat.shape) == (S, NH, KVL) and lat.is_contiguous(), ValueError, "dbg lat")
+        _need(codes.dtype == torch.uint8 and tuple(codes.shape) == (S, NH, KVL // 2) and codes.is_contiguous(), ValueError, "dbg codes")
+        _need(scales.dtype == torch.uint8 and tuple(scales.shape) == (S, NH, KVL // 32) and scales.is_contiguous(), ValueError, "dbg scales")
+        a.dbg_lat, a.dbg_codes, a.dbg_scales = lat.data_ptr(), codes.data_ptr(), scales.data_ptr()
+    return a
+
+
+def mla_post(o, lse, w_v, w_v_scale, gate, core=None, debug: bool = False):
+    """One mla_post call on torch's current stream of core's device.
+
+    Returns core (bf16 [S, 1536]); with ``debug=True`` returns
+    (core, latents bf16 [S,12,512], codes u8 [S,12,256], scales u8 [S,12,16]),
+    all written by the same kernel launch.
+    """
+    lib = load()
+    S = int(o.shape[1])
+    if core is None:
+        core = torch.empty((S, GROWS), dtype=torch.bfloat16, device=gate.device)
+    dbg = None
+    if debug:
+        dev = core.device
+        dbg = (
+            torch.empty((S, NH, KVL), dtype=torch.bfloat16, device=dev),
+            torch.empty((S, NH, KVL // 2), dtype=torch.uint8, device=dev),
+            torch.empty((S, NH, KVL // 32), dtype=torch.uint8, device=dev),
+        )
+    a = make_args(o, lse, w_v, w_v_scale, gate, core, dbg)
+    _need(core.is_cuda, ValueError, "tensors must be on a GPU")
+    _raise(lib, lib.mla_post(ctypes.byref(a), ctypes.c_void_p(_stream(core.device))))
+    return core if not debug else (core,) + dbg
+
+
+def mla_post_splits(o, lse, w_v, w_v_scale, gate, core=None, debug=False):
+    """Split-KV partials: o [P, S, 12, 512], lse [P, S, 12] (token t merges o[:, t])."""
+    return mla_post(o, lse, w_v, w_v_scale, gate, core, debug)
+
+
+def ranks_view(o_gathered, lse_gathered, ranks: int):
+    """Views [R, S, 12, 512] / [R, S, 12] of decode-context-parallel partials
+    gathered as o [S, >= R*12, 512] and lse [S, >= R*12]: rank r's partial of
+    local head h is gathered head r*12 + h (the page's mla_post layout)."""
+    S = o_gathered.shape[0]
+    _need(o_gathered.shape[1] >= ranks * NH and o_gathered.shape[2] == KVL, ValueError, "o must be [S, >= R*12, 512]")
+    so = o_gathered.stride()
+    ov = o_gathered.as_strided((ranks, S, NH, KVL), (NH * so[1], so[0], so[1], so[2]), o_gathered.storage_offset())
+    lv = None
+    if lse_gathered is not None:
+        sl = lse_gathered.stride()
+        lv = lse_gathered.as_strided((ranks, S, NH), (NH * sl[1], sl[0], sl[1]), lse_gathered.storage_offset())
+    return ov, lv
+
+
+def mla_post_ranks(o_gathered, lse_gathered, ranks: int, w_v, w_v_scale, gate, core=None, debug=False):
+    """Decode-context-parallel merge of R gathered rank partials, in rank order."""
+    ov, lv = ranks_view(o_gathered, lse_gathered, ranks)
+    return mla_post(ov, lv, w_v, w_v_scale, gate, core, debug)
+
+
+def quantize_mxfp4(x):
+    """bf16 [rows, cols] (cols % 32 == 0, innermost stride 1) -> (codes uint8
+    [rows, cols/2], scales uint8 [rows, cols/32]) with the kernel's own rule."""
+    lib = load()
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1, TypeError, "x must be bf16 [rows, cols]")
+    rows, cols = int(x.shape[0]), int(x.shape[1])
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    st = lib.mla_quantize_mxfp4(
+        ctypes.c_void_p(x.data_ptr()),
+        rows,
+        cols,
+        x.stride(0),
+        ctypes.c_void_p(codes.data_ptr()),
+        codes.stride(0),
+        ctypes.c_void_p(scales.data_ptr()),
+        scales.stride(0),
+        ctypes.c_void_p(_stream(x.device)),
+    )
+    _raise(lib, st)
+    return codes, scales

@@ -1,0 +1,63 @@
+"""Build libmla_post.so in-tree with hipcc for gfx950.
+
+    python -m mla_split_kv_amd.build
+
+Compiles every time it is called (the C-ABI library, its kernels and host code
+from csrc/mla_post.hip). Packed-FP32 instructions are disabled for the device
+code; hipcc's host pass warns that it does not know that feature, harmlessly.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "mla_post.hip")
+INC = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmla_post.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found")
+    return p
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [
+        hipcc(),
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-Xclang",
+        "-target-feature",
+        "-Xclang",
+        "-packed-fp32-ops",
+        "-I",
+        INC,
+        "-o",
+        tmp,
+        SRC,
+    ]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
+    if verbose and msg.strip():
+        print(msg, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,463 @@
+// mla_post: fused MLA decode post-attention for AMD MI355X (gfx950 / CDNA4).
+//
+// One launch does the whole path the vLLM API-docs page for module
+// vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_back
+// describes (module docstring; stage_combine, combine_splits, combine_ranks,
+// sane, stage_uv, wv_loads): LSE merge of bf16 partial rows -> bf16 latents
+// -> MXFP4 -> scaled FP4 MFMA against W_V[h] -> bf16 x gate -> core.
+//
+// Decomposition (this library's own, not the page's):
+//   workgroup = (head h, 16 tokens), 8 waves of 64 lanes;
+//   merge: wave w owns tokens 2w and 2w+1 of the tile; a token's partial row
+//     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced 16-byte load
+//     per lane, and a wave keeps ROWS_IN_FLIGHT rows in flight;
+//   the merged latents never go to memory: each lane rounds its 8 latents
+//     to bf16, the 4 lanes of a 32-element block agree on the E8M0 code with
+//     two DPP steps, and the hardware scaled convert packs the 8 FP4 codes;
+//     codes and scales are staged in LDS as the MFMA B operand;
+//   W_UV: wave w multiplies W_V[h] rows 16w..16w+15 (A operand, prefetched
+//     into registers before the merge) by the 16 tokens' latent codes, four
+//     16x16x128 scaled FP4 MFMAs over K = 512, so all 16 MFMA columns carry
+//     live tokens (the page fills 4 of 16);
+//   epilogue: bf16(acc) x gate -> bf16, 8-byte stores, tokens < S only.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <string>
+
+#include "mla_post.h"
+
+namespace {
+
+constexpr int NH = MLA_POST_HEADS;
+constexpr int KVL = MLA_POST_KVL;
+constexpr int VD = MLA_POST_VD;
+constexpr int GROWS = MLA_POST_GROWS;
+constexpr int TILE_T = 16;                     // tokens per workgroup (MFMA N)
+constexpr int WAVES = VD / 16;                 // 8 waves x 16 W_V rows
+constexpr int THREADS = WAVES * 64;            // 512
+constexpr int TOK_PER_WAVE = TILE_T / WAVES;   // 2
+constexpr int ROWS_IN_FLIGHT = 8;              // partial rows a wave loads before it sums
+constexpr int NBLK = KVL / 32;                 // 16 MXFP4 blocks per latent row
+constexpr int CODE_ROW = TILE_T * 16 + 16;     // LDS bytes per block row (+16 B skew)
+constexpr int LDS_CODES = NBLK * CODE_ROW;     // 4352 B
+constexpr int LDS_SCALES = TILE_T * NBLK;      // 256 B
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+struct KArgs {
+  const uint8_t* o;
+  int64_t o_sj, o_st, o_sh;  // bytes
+  const float* lse;
+  int64_t l_sj, l_st, l_sh;  // elements
+  const uint8_t* w_v;
+  int64_t w_sh, w_sv;
+  const uint8_t* w_vs;
+  int64_t s_sh, s_sv, s_sb;
+  const uint8_t* gate;
+  uint8_t* core;
+  uint8_t* dbg_lat;
+  uint8_t* dbg_codes;
+  uint8_t* dbg_scales;
+  int32_t n, S;
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two float32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float round_bf16(float x) {
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) << 16);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// LSE NaN / +inf -> -inf ([mla_back: sane]).
+__device__ __forceinline__ float sane(float x) { return (x != x || x == INFINITY) ? -INFINITY : x; }
+
+// MXFP4 quantisation of the 8 bf16 latents a lane holds (4 packed words);
+// lanes 4b .. 4b+3 hold the 32 elements of block b. Returns the 8 E2M1
+// codes (element 2i in the low nibble of byte i) and the block's E8M0 code.
+// Scale code: max(1, ((amax_bits + 0x20) >> 7) - 2) over the 15-bit bf16
+// magnitude patterns; the conversion divides by 2^(code-127) and rounds to
+// nearest even with saturation (v_cvt_scalef32_pk_fp4_bf16).
+__device__ __forceinline__ uint32_t quant8(const uint32_t w[4], int& code_out) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    am = max(am, w[i] & 0x7FFFu);
+    am = max(am, (w[i] >> 16) & 0x7FFFu);
+  }
+  // quad reduction: xor 1 (quad_perm [1,0,3,2]) then xor 2 ([2,3,0,1])
+  am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
+  am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x4E, 0xF, 0xF, false));
+  int code = max((int)((am + 0x20u) >> 7) - 2, 1);
+  float scale = __uint_as_float((uint32_t)code << 23);
+  int pk = 0;
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, __builtin_bit_cast(bf2, w[0]), scale, 0);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, __builtin_bit_cast(bf2, w[1]), scale, 1);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, __builtin_bit_cast(bf2, w[2]), scale, 2);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, __builtin_bit_cast(bf2, w[3]), scale, 3);
+  code_out = code;
+  return (uint32_t)pk;
+}
+
+template <int ST>
+__device__ __forceinline__ v4f mfma_step(const uint4& a, const uint4& b, v4f acc, int sa, int sb) {
+  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  // formats 4/4 = FP4 E2M1 for A and B; opsel ST picks byte ST of each scale word
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, ST, sa, ST, sb);
+}
+
+// LSE weights of one (t, h): lane j of chunk c holds w_{64c + j}.
+// [mla_back: combine_splits] / [mla_back: combine_ranks]: m = max, 0 when all
+// are -inf; e = exp(lse - m); weight e / sum, 0 when e == 0 or the sum is 0.
+template <int NCH>
+__device__ __forceinline__ void lse_weights(const KArgs& a, int t, int h, int lane, float wts[NCH]) {
+  float l[NCH];
+  float m = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int j = 64 * c + lane;
+    float x = -INFINITY;
+    if (j < a.n) x = sane(a.lse[(int64_t)j * a.l_sj + (int64_t)t * a.l_st + (int64_t)h * a.l_sh]);
+    l[c] = x;
+    m = fmaxf(m, x);
+  }
+  m = wave_max(m);
+  if (m == -INFINITY) m = 0.f;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    l[c] = expf(l[c] - m);
+    s += l[c];
+  }
+  float tot = wave_sum(s);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) wts[c] = (tot == 0.f || l[c] == 0.f) ? 0.f : l[c] / tot;
+}
+
+// Weighted sum of the partial rows of (t, h) for this lane's 8 latents
+// [k = 8 lane .. 8 lane + 7], skipping rows of weight 0 (not even loaded).
+template <int NCH>
+__device__ __forceinline__ void merge_rows(const KArgs& a, const uint8_t* rowbase, int lane, const float wts[NCH],
+                                           float acc[8]) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int nc = min(64, a.n - 64 * c);
+    const int wbits = __float_as_int(wts[c]);
+    for (int j0 = 0; j0 < nc; j0 += ROWS_IN_FLIGHT) {
+      uint4 v[ROWS_IN_FLIGHT];
+      float wj[ROWS_IN_FLIGHT];
+#pragma unroll
+      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) {
+        const int jl = j0 + b;
+        int wb = __builtin_amdgcn_readlane(wbits, jl & 63);
+        if (jl >= nc) wb = 0;
+        wj[b] = __int_as_float(wb);
+        v[b] = make_uint4(0, 0, 0, 0);
+        if (wb & 0x7FFFFFFF) {
+          const uint8_t* p = rowbase + (int64_t)(64 * c + jl) * a.o_sj;
+          v[b] = reinterpret_cast<const uint4*>(p)[lane];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) {
+        const float w = wj[b];
+        acc[0] = fmaf(w, bf_lo(v[b].x), acc[0]);
+        acc[1] = fmaf(w, bf_hi(v[b].x), acc[1]);
+        acc[2] = fmaf(w, bf_lo(v[b].y), acc[2]);
+        acc[3] = fmaf(w, bf_hi(v[b].y), acc[3]);
+        acc[4] = fmaf(w, bf_lo(v[b].z), acc[4]);
+        acc[5] = fmaf(w, bf_hi(v[b].z), acc[5]);
+        acc[6] = fmaf(w, bf_lo(v[b].w), acc[6]);
+        acc[7] = fmaf(w, bf_hi(v[b].w), acc[7]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- the fused kernel
+
+template <bool NOLSE, int NCH>
+__global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.x % NH;
+  const int t0 = (blockIdx.x / NH) * TILE_T;
+  const int tl = lane & 15;  // MFMA row / column index of this lane
+  const int kb = lane >> 4;  // MFMA K block of this lane
+
+  // W_V[h] rows wave*16 + tl, K block kb of each of the 4 K steps
+  // ([mla_back: wv_loads]): issued first, consumed after the merge.
+  uint4 wv[4];
+  int sa = 0;
+  {
+    const int v = wave * 16 + tl;
+    const uint8_t* wrow = a.w_v + h * a.w_sh + v * a.w_sv + kb * 16;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) wv[st] = *reinterpret_cast<const uint4*>(wrow + st * 64);
+    const uint8_t* srow = a.w_vs + h * a.s_sh + v * a.s_sv;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) sa |= (int)srow[(st * 4 + kb) * a.s_sb] << (8 * st);
+  }
+
+  // ---- merge + quantise: wave owns tokens t0 + 2 wave, t0 + 2 wave + 1
+#pragma unroll 1
+  for (int i = 0; i < TOK_PER_WAVE; ++i) {
+    const int tt = wave * TOK_PER_WAVE + i;
+    const int t = t0 + tt;
+    uint32_t lat[4] = {0u, 0u, 0u, 0u};
+    const bool live = t < a.S;
+    if (live) {
+      const uint8_t* rowbase = a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
+      if constexpr (NOLSE) {
+        // one partial and no LSE: the row is the attention output itself
+        uint4 v = reinterpret_cast<const uint4*>(rowbase)[lane];
+        lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+      } else {
+        float wts[NCH];
+        lse_weights<NCH>(a, t, h, lane, wts);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        merge_rows<NCH>(a, rowbase, lane, wts, acc);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
+      }
+    }
+    int code;
+    uint32_t pk = quant8(lat, code);
+    const int b = lane >> 2;  // this lane's block
+    *reinterpret_cast<uint32_t*>(s_codes + b * CODE_ROW + tt * 16 + (lane & 3) * 4) = live ? pk : 0u;
+    if ((lane & 3) == 0) s_scales[tt * NBLK + (b & 3) * 4 + (b >> 2)] = (uint8_t)code;
+    if (live) {
+      const int64_t th = (int64_t)t * NH + h;
+      if (a.dbg_lat)
+        reinterpret_cast<uint4*>(a.dbg_lat + th * (KVL * 2))[lane] = make_uint4(lat[0], lat[1], lat[2], lat[3]);
+      if (a.dbg_codes) reinterpret_cast<uint32_t*>(a.dbg_codes + th * (KVL / 2))[lane] = pk;
+      if (a.dbg_scales && (lane & 3) == 0) a.dbg_scales[th * NBLK + b] = (uint8_t)code;
+    }
+  }
+  __syncthreads();
+
+  // ---- W_UV: D[v][token] = sum_k W_V[h][v][k] * L[token][k]
+  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const uint8_t* brow = s_codes + tl * 16;
+    acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
+  }
+  // The MFMAs read operands from all 64 lanes: they must run with the whole
+  // wave active. Pinning the result here keeps the compiler from sinking them
+  // into the per-lane store condition below (where a ragged tile masks lanes).
+  asm volatile("" : "+v"(acc));
+
+  // ---- gate and store ([mla_back: stage_uv]): lane holds rows v0..v0+3 of token tl
+  const int t = t0 + tl;
+  if (t < a.S) {
+    const int col = h * VD + wave * 16 + kb * 4;
+    const int64_t off = ((int64_t)t * GROWS + col) * 2;
+    const uint2 g = *reinterpret_cast<const uint2*>(a.gate + off);
+    const float o0 = round_bf16(acc[0]) * bf_lo(g.x);
+    const float o1 = round_bf16(acc[1]) * bf_hi(g.x);
+    const float o2 = round_bf16(acc[2]) * bf_lo(g.y);
+    const float o3 = round_bf16(acc[3]) * bf_hi(g.y);
+    *reinterpret_cast<uint2*>(a.core + off) = make_uint2(pack_bf16(o0, o1), pack_bf16(o2, o3));
+  }
+}
+
+// ---------------------------------------------------------------- stand-alone quantiser
+
+constexpr int QWAVES = 4;
+
+__global__ __launch_bounds__(QWAVES * 64) void quantize_kernel(const uint8_t* x, int64_t rows, int cols,
+                                                               int64_t xs_bytes, uint8_t* codes, int64_t cs,
+                                                               uint8_t* scales, int64_t ss) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole wave
+  for (int c0 = 0; c0 < cols; c0 += 512) {
+    const int c = c0 + lane * 8;
+    const bool in = c < cols;  // cols is a multiple of 32: whole quads are in or out
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (in) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + r * xs_bytes + (int64_t)c * 2);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+    int code;
+    const uint32_t pk = quant8(w, code);
+    if (in) {
+      *reinterpret_cast<uint32_t*>(codes + r * cs + c / 2) = pk;
+      if ((lane & 3) == 0) scales[r * ss + c / 32] = (uint8_t)code;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+thread_local std::string g_hip_error;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow(a, b, out); }
+
+// largest byte offset reached by index (n0-1, n1-1, n2-1) with the given byte strides, plus `tail`
+bool span_ok(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t s2, int64_t tail) {
+  int64_t a, b, c, x, y;
+  return mul_ok(n0 - 1, s0, &a) && mul_ok(n1 - 1, s1, &b) && mul_ok(n2 - 1, s2, &c) && add_ok(a, b, &x) &&
+         add_ok(x, c, &y) && add_ok(y, tail, &x);
+}
+
+bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
+
+int check_args(const mla_post_args* a) {
+  if (!a || a->struct_size < sizeof(mla_post_args)) return MLA_POST_EINVAL;
+  if (a->n < 1 || a->S < 0) return MLA_POST_EINVAL;
+  if (a->n > MLA_POST_NMAX) return MLA_POST_EUNSUPPORTED;
+  if (a->S == 0) return MLA_POST_OK;
+  if (!a->o || !a->w_v || !a->w_v_scale || !a->gate || !a->core) return MLA_POST_EINVAL;
+  if (!a->lse && a->n != 1) return MLA_POST_EINVAL;
+  if (a->o_sj < 0 || a->o_st < 0 || a->o_sh < 0) return MLA_POST_ESTRIDE;
+  if ((a->o_sj % 8) || (a->o_st % 8) || (a->o_sh % 8)) return MLA_POST_ESTRIDE;
+  if (a->lse && (a->l_sj < 0 || a->l_st < 0 || a->l_sh < 0)) return MLA_POST_ESTRIDE;
+  if (a->w_sh < 0 || a->w_sv < 0 || (a->w_sh % 16) || (a->w_sv % 16)) return MLA_POST_ESTRIDE;
+  if (a->s_sh < 0 || a->s_sv < 0 || a->s_sb < 0) return MLA_POST_ESTRIDE;
+  if (!aligned(a->o, 16) || !aligned(a->w_v, 16) || !aligned(a->gate, 8) || !aligned(a->core, 8))
+    return MLA_POST_EALIGN;
+  if (a->lse && !aligned(a->lse, 4)) return MLA_POST_EALIGN;
+  if ((a->dbg_lat && !aligned(a->dbg_lat, 16)) || (a->dbg_codes && !aligned(a->dbg_codes, 4))) return MLA_POST_EALIGN;
+  // every byte offset the kernel forms must fit int64
+  int64_t bsj, bst, bsh;
+  if (!mul_ok(a->o_sj, 2, &bsj) || !mul_ok(a->o_st, 2, &bst) || !mul_ok(a->o_sh, 2, &bsh) ||
+      !span_ok(a->n, bsj, a->S, bst, NH, bsh, KVL * 2))
+    return MLA_POST_ERANGE;
+  if (a->lse && (!mul_ok(a->l_sj, 4, &bsj) || !mul_ok(a->l_st, 4, &bst) || !mul_ok(a->l_sh, 4, &bsh) ||
+                 !span_ok(a->n, bsj, a->S, bst, NH, bsh, 4)))
+    return MLA_POST_ERANGE;
+  if (!span_ok(NH, a->w_sh, VD, a->w_sv, 1, 0, KVL / 2)) return MLA_POST_ERANGE;
+  if (!span_ok(NH, a->s_sh, VD, a->s_sv, NBLK, a->s_sb, 1)) return MLA_POST_ERANGE;
+  if (!span_ok(a->S, (int64_t)GROWS * 2, 1, 0, 1, 0, GROWS * 2)) return MLA_POST_ERANGE;
+  return MLA_POST_OK;
+}
+
+template <bool NOLSE, int NCH>
+int launch(const KArgs& k, int S, hipStream_t stream) {
+  const unsigned grid = (unsigned)(NH * ((S + TILE_T - 1) / TILE_T));
+  hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_hip_error = hipGetErrorString(e);
+    return MLA_POST_ELAUNCH;
+  }
+  return MLA_POST_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_post_check(const mla_post_args* a) { return check_args(a); }
+
+int mla_post(const mla_post_args* a, void* stream) {
+  const int st = check_args(a);
+  if (st != MLA_POST_OK || a->S == 0) return st;
+  KArgs k;
+  k.o = static_cast<const uint8_t*>(a->o);
+  k.o_sj = a->o_sj * 2;
+  k.o_st = a->o_st * 2;
+  k.o_sh = a->o_sh * 2;
+  k.lse = a->lse;
+  k.l_sj = a->l_sj;
+  k.l_st = a->l_st;
+  k.l_sh = a->l_sh;
+  k.w_v = a->w_v;
+  k.w_sh = a->w_sh;
+  k.w_sv = a->w_sv;
+  k.w_vs = a->w_v_scale;
+  k.s_sh = a->s_sh;
+  k.s_sv = a->s_sv;
+  k.s_sb = a->s_sb;
+  k.gate = static_cast<const uint8_t*>(a->gate);
+  k.core = static_cast<uint8_t*>(a->core);
+  k.dbg_lat = static_cast<uint8_t*>(a->dbg_lat);
+  k.dbg_codes = static_cast<uint8_t*>(a->dbg_codes);
+  k.dbg_scales = static_cast<uint8_t*>(a->dbg_scales);
+  k.n = a->n;
+  k.S = a->S;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!a->lse) return launch<true, 1>(k, a->S, s);
+  if (a->n <= 64) return launch<false, 1>(k, a->S, s);
+  if (a->n <= 128) return launch<false, 2>(k, a->S, s);
+  if (a->n <= 256) return launch<false, 4>(k, a->S, s);
+  return launch<false, 8>(k, a->S, s);
+}
+
+int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stride, uint8_t* codes, int64_t c_stride,
+                       uint8_t* scales, int64_t s_stride, void* stream) {
+  if (rows < 0 || cols < 0) return MLA_POST_EINVAL;
+  if (rows == 0 || cols == 0) return MLA_POST_OK;
+  if (!x || !codes || !scales) return MLA_POST_EINVAL;
+  if ((cols % 32) || cols > 8192) return MLA_POST_EUNSUPPORTED;
+  if (x_stride < 0 || c_stride < 0 || s_stride < 0 || (x_stride % 8) || (c_stride % 4)) return MLA_POST_ESTRIDE;
+  if (!aligned(x, 16) || !aligned(codes, 4)) return MLA_POST_EALIGN;
+  int64_t xsb;
+  if (!mul_ok(x_stride, 2, &xsb) || !span_ok(rows, xsb, 1, 0, 1, 0, (int64_t)cols * 2) ||
+      !span_ok(rows, c_stride, 1, 0, 1, 0, cols / 2) ||
+      !span_ok(rows, s_stride, 1, 0, 1, 0, cols / 32))
+    return MLA_POST_ERANGE;
+  const int64_t blocks = (rows + QWAVES - 1) / QWAVES;
+  if (blocks > 0x7FFFFFFF) return MLA_POST_ERANGE;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(x), rows, cols, x_stride * 2, codes, c_stride, scales, s_stride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_hip_error = hipGetErrorString(e);
+    return MLA_POST_ELAUNCH;
+  }
+  return MLA_POST_OK;
+}
+
+const char* mla_post_strerror(int status) {
+  switch (status) {
+    case MLA_POST_OK: return "ok";
+    case MLA_POST_EINVAL: return "invalid argument (null pointer, size out of range, or lse NULL with n > 1)";
+    case MLA_POST_ESTRIDE: return "stride negative or not a multiple the vector loads need";
+    case MLA_POST_EALIGN: return "pointer not aligned for its vector loads or stores";
+    case MLA_POST_ERANGE: return "an operand's byte offsets overflow 64-bit arithmetic";
+    case MLA_POST_EUNSUPPORTED: return "unsupported size (n above MLA_POST_NMAX, or cols not a multiple of 32)";
+    case MLA_POST_ELAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_post_last_hip_error(void) { return g_hip_error.c_str(); }
+
+int mla_post_version(void) { return MLA_POST_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,249 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Every input is seeded and synthetic (synth.workloads); W_V is put into MXFP4
+by the oracle's quantiser. Stage outputs (latents, codes, scales) come from
+the same kernel launch as core. Criteria T1-T4 are defined in criteria.py.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import criteria as C
+import oracle.post as O
+import synth
+from gpu_support import bf16_to_dev, device_inputs, run_debug, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def full_parity(m, w, strict_t4=False, tokens=None):
+    """Run w on the GPU with stage outputs and check T1-T4 on all tokens (or
+    the given sample); returns the statistics."""
+    say(f"{w.name}: n={w.n} S={w.S} strides={w.o_strides}")
+    d = device_inputs(w)
+    g = run_debug(m, d)
+    ref = O.mla_post(w.o_view(), w.lse_view(), d["w_codes"], d["w_scales"], w.gate, tokens=tokens)
+    sel = slice(None) if tokens is None else np.asarray(tokens)
+    lat, codes, scales, core = g["lat"][sel], g["codes"][sel], g["scales"][sel], g["core"][sel]
+    stats = {}
+    stats.update(C.check_t1(lat, ref, exact=w.lse_buf is None))
+    stats.update(C.check_t2(lat, codes, scales))
+    stats.update(C.check_t3(core, codes, scales, d["w_codes"], d["w_scales"], w.gate[sel]))
+    stats.update(C.check_t4(core, ref, lat, codes, scales, strict=strict_t4))
+    say(f"{w.name}: {stats}")
+    return stats, g, d
+
+
+# ---------------------------------------------------------------- the five standard workloads
+
+
+def test_tiny(gpu_lib):
+    full_parity(gpu_lib, synth.tiny(), strict_t4=True)
+
+
+def test_no_merge(gpu_lib):
+    full_parity(gpu_lib, synth.no_merge(), strict_t4=True)
+
+
+def test_split_merge(gpu_lib):
+    full_parity(gpu_lib, synth.split_merge())
+
+
+def test_dcp8(gpu_lib):
+    stats, g, _ = full_parity(gpu_lib, synth.dcp8())
+    # tokens >= 240 have every LSE -inf: exact zeros
+    assert np.all(g["core"][240:] == 0) and np.all(g["lat"][240:] == 0)
+
+
+def test_large_decode_sampled(gpu_lib):
+    """Full-size large decode batch (805 MB of partials), launched as the
+    benchmark launches it (no stage outputs) and with stage outputs: core is
+    bit-identical between the two; T2 on every block of the full size; T1,
+    T3, T4 on a sample of tokens from every part of the batch."""
+    m = gpu_lib
+    w = synth.large_decode()
+    say(f"{w.name}: n={w.n} S={w.S}")
+    d = device_inputs(w)
+    core_plain = m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"])
+    torch.cuda.synchronize()
+    g = run_debug(m, d)
+    assert np.array_equal(to_bits(core_plain), g["core"]), "stage outputs changed core"
+    for s0 in range(0, w.S, 512):  # T2 on all 786k blocks, in slices
+        C.check_t2(g["lat"][s0 : s0 + 512], g["codes"][s0 : s0 + 512], g["scales"][s0 : s0 + 512])
+    rng = np.random.default_rng(7)
+    tokens = np.unique(np.concatenate([[0, 1, 15, 16, w.S - 1], rng.integers(0, w.S, size=43)]))
+    ref = O.mla_post(w.o_view(), w.lse_view(), d["w_codes"], d["w_scales"], w.gate, tokens=tokens)
+    st = {}
+    st.update(C.check_t1(g["lat"][tokens], ref))
+    st.update(C.check_t3(g["core"][tokens], g["codes"][tokens], g["scales"][tokens], d["w_codes"], d["w_scales"], w.gate[tokens]))
+    st.update(C.check_t4(g["core"][tokens], ref, g["lat"][tokens], g["codes"][tokens], g["scales"][tokens]))
+    say(f"{w.name}: sampled {len(tokens)} tokens {st}")
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize(
+    "w",
+    [
+        pytest.param(lambda: synth.dense_splits("ragged_S37", 3, 37, seed=10, p_neg_inf=0.2), id="ragged_S37"),
+        pytest.param(lambda: synth.dense_splits("S1", 5, 1, seed=15), id="S1"),
+        pytest.param(lambda: synth.dense_splits("n1_with_lse", 1, 19, seed=13, p_neg_inf=0.3, p_nan=0.1, p_pos_inf=0.1), id="n1_lse"),
+        pytest.param(lambda: synth.dense_splits("n65", 65, 9, seed=11, p_neg_inf=0.1), id="n65_two_chunks"),
+        pytest.param(lambda: synth.dense_splits("n300", 300, 3, seed=12, p_neg_inf=0.5), id="n300_eight_chunks"),
+        pytest.param(lambda: synth.dense_splits("nmax", 512, 2, seed=16, p_neg_inf=0.05), id="n_max_512"),
+        pytest.param(lambda: synth.dense_splits("all_dead", 4, 20, seed=14, p_neg_inf=1.0), id="all_dead"),
+        pytest.param(lambda: synth.dense_splits("wide_lse", 12, 24, seed=17, lse_normal=(0.0, 80.0)), id="wide_lse_spread"),
+        pytest.param(lambda: synth.dcp_gathered("dcp3_pad", 3, 29, seed=18, head_stride_rows=40, dead_from=20), id="dcp3_padded"),
+        pytest.param(lambda: synth.single_partial("no_merge_S5", 5, seed=19, o_sigma=300.0), id="no_merge_ragged"),
+    ],
+)
+def test_edge(gpu_lib, w):
+    w = w()
+    stats, g, _ = full_parity(gpu_lib, w, strict_t4=(w.n <= 1 and w.lse_buf is None))
+    if w.name == "all_dead":
+        assert np.all(g["core"] == 0) and np.all(g["lat"] == 0) and np.all(g["scales"] == 1)
+
+
+def test_dead_rows_nan_inf_not_read(gpu_lib):
+    """Rows of weight 0 hold NaN and inf: the result equals the oracle's, which
+    never touches them, and is finite."""
+    w = synth.dense_splits("poisoned_dead", 6, 40, seed=20, p_neg_inf=0.2, p_nan=0.1, p_pos_inf=0.1)
+    lse = w.lse_view()
+    dead = ~np.isfinite(lse)
+    ob = w.o_buf.copy()
+    ob[dead] = np.where(np.arange(512) % 2 == 0, 0x7FC0, 0x7F80).astype(np.uint16)
+    w.o_buf = ob
+    stats, g, _ = full_parity(gpu_lib, w)
+    assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
+
+
+def test_strided_weights_and_lse(gpu_lib):
+    """W_V codes as a column slice of a wider buffer, scales stored with the
+    block axis outermost, lse as a non-dense view: same result as the dense
+    layout, and equal to the oracle."""
+    m = gpu_lib
+    w = synth.dense_splits("strided", 4, 33, seed=21, p_neg_inf=0.1)
+    d = device_inputs(w)
+    base = run_debug(m, d)
+    wide = torch.zeros((12, 128, 512), dtype=torch.uint8, device="cuda")
+    wide[:, :, 128:384] = d["w_v"]
+    w_v = wide[:, :, 128:384]
+    sc_t = d["w_v_scale"].permute(2, 0, 1).contiguous()  # [16, 12, 128]
+    w_s = sc_t.permute(1, 2, 0)  # logical [12, 128, 16], strides (128, 1, 1536)
+    lse_wide = torch.full((4, 33, 12, 3), float("nan"), device="cuda")
+    lse_wide[..., 1] = d["lse"]
+    lse_v = lse_wide[..., 1]
+    say("strided: w_v slice, scales block-major, lse stride 3")
+    core, lat, codes, scales = m.mla_post(d["o"], lse_v, w_v, w_s, d["gate"], debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(core), base["core"])
+    assert np.array_equal(to_bits(lat), base["lat"])
+    full_parity(m, w)
+
+
+def test_canary_and_coverage(gpu_lib):
+    """core is written for every token < S and nowhere else: rows around it
+    keep their canary, and no poisoned element survives inside."""
+    m = gpu_lib
+    w = synth.dense_splits("canary", 3, 21, seed=22, p_neg_inf=0.1)
+    d = device_inputs(w)
+    buf = torch.full((w.S + 2, 1536), 0, dtype=torch.int16, device="cuda")
+    buf[0] = 0x7E57
+    buf[-1] = 0x7E57
+    buf[1:-1] = -1  # 0xFFFF, a NaN pattern the kernel never writes
+    core = buf[1:-1].view(torch.bfloat16)
+    say("canary")
+    m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], core=core)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy().view(np.uint16)
+    assert np.all(h[0] == 0x7E57) and np.all(h[-1] == 0x7E57)
+    assert not np.any(h[1:-1] == 0xFFFF)
+
+
+def test_empty_batch_is_noop(gpu_lib):
+    m = gpu_lib
+    say("S=0")
+    o = torch.zeros((2, 0, 12, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((2, 0, 12), dtype=torch.float32, device="cuda")
+    w_v = torch.zeros((12, 128, 256), dtype=torch.uint8, device="cuda")
+    w_s = torch.full((12, 128, 16), 127, dtype=torch.uint8, device="cuda")
+    gate = torch.zeros((0, 1536), dtype=torch.bfloat16, device="cuda")
+    core = m.mla_post(o, lse, w_v, w_s, gate)
+    torch.cuda.synchronize()
+    assert core.shape == (0, 1536)
+
+
+def test_deterministic(gpu_lib):
+    """Two launches give bit-identical core."""
+    m = gpu_lib
+    w = synth.split_merge()
+    d = device_inputs(w)
+    say("determinism")
+    a = to_bits(m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"]))
+    b = to_bits(m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"]))
+    assert np.array_equal(a, b)
+
+
+def test_ranks_helper_matches_view(gpu_lib):
+    """mla_post_ranks on the gathered [S, 104, 512] buffer equals mla_post on
+    the explicit [R, S, 12, 512] view."""
+    m = gpu_lib
+    w = synth.dcp8()
+    d = device_inputs(w)
+    ob = d["o_buf"]  # [256, 104, 512]
+    lse_g = torch.from_numpy(w.lse_buf).cuda()  # [256, 96]
+    say("ranks helper")
+    a = to_bits(m.mla_post_ranks(ob, lse_g, 8, d["w_v"], d["w_v_scale"], d["gate"]))
+    b = to_bits(m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"]))
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- the stand-alone quantiser
+
+
+def test_quantizer_exhaustive(gpu_lib):
+    """The device quantiser equals the oracle's on every bf16 pattern (each in
+    blocks with different maxima), bit for bit."""
+    m = gpu_lib
+    say("quantiser exhaustive")
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]  # finite patterns
+    rng = np.random.default_rng(30)
+    for perm in range(3):
+        x = rng.permutation(b) if perm else b.copy()
+        pad = (-x.size) % 512
+        x = np.concatenate([x, np.zeros(pad, np.uint16)]).reshape(-1, 512)
+        codes, scales = m.quantize_mxfp4(bf16_to_dev(x, "cuda"))
+        torch.cuda.synchronize()
+        rc, rs = O.quantize_mxfp4(x)
+        assert np.array_equal(scales.cpu().numpy(), rs)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+    # odd widths and a strided input
+    x = O.rne_bf16(rng.standard_normal((37, 96)) * 3.0)
+    wide = bf16_to_dev(np.concatenate([x, x], axis=1), "cuda")
+    codes, scales = m.quantize_mxfp4(wide[:, :96])
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_mxfp4(x)
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_quantizer_wv_matches_oracle(gpu_lib):
+    """W_V put into MXFP4 on the GPU equals the oracle's encoding."""
+    m = gpu_lib
+    w = synth.tiny()
+    say("quantiser W_V")
+    codes, scales = m.quantize_mxfp4(bf16_to_dev(w.wv_bits.reshape(-1, 512), "cuda"))
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_mxfp4(w.wv_bits)
+    assert np.array_equal(codes.cpu().numpy().reshape(rc.shape), rc)
+    assert np.array_equal(scales.cpu().numpy().reshape(rs.shape), rs)
