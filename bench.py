@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of mla_post on one MI355X.
+
+A step is one mla_post call over one batch: the whole path (LSE merge of the
+bf16 partial rows, bf16 latents, MXFP4, FP4-MFMA W_UV, gate) in the fused
+kernel, with every input already resident in HBM. The workload is the large
+decode batch: S = 4096 tokens (1024 requests x 4), 16 KV splits per request,
+12 heads, latent 512, o ~ N(0, 2) bf16 [16, 4096, 12, 512] (805 MB),
+lse ~ N(8, 6) with 5% -inf, W_V ~ N(0, 1/sqrt(512)) put into MXFP4 by the
+library's quantiser, gate ~ U(0, 1) bf16. Inputs are seeded and synthetic.
+
+Prints one JSON line: tokens/s (whole job), ms per step, the roofline of the
+fused kernel (algorithmic HBM bytes per launch / its average duration from HIP
+events over the timed region, against 8 TB/s) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --calibrate-copy   # a plain 1 GiB device copy, for counter scaling
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+KERNEL_SRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc", "mla_post.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_post_large_decode.json")
+W_V_BYTES = 12 * 128 * 256 + 12 * 128 * 16  # MXFP4 codes + E8M0 scales, read once per launch
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes the method must move per call: each partial row of non-zero
+    weight (1 KiB, rows whose LSE is -inf, NaN or +inf are not read), every
+    LSE (4 B), W_V once, the gate read and the core write (S x 1536 bf16 each)."""
+    import synth
+
+    live = synth.live_rows(w)
+    n_lse = 0 if w.lse_buf is None else w.n * w.S * 12
+    gate_core = 2 * w.S * 1536 * 2
+    live_b = live * 1024 + n_lse * 4 + W_V_BYTES + gate_core
+    nominal_b = w.n * w.S * 12 * 1024 + n_lse * 4 + W_V_BYTES + gate_core
+    return {"live_rows": live, "rows": w.n * w.S * 12, "alg_bytes": live_b, "nominal_bytes": nominal_b}
+
+
+def device_setup(w, m, torch):
+    """Move a workload to the GPU; W_V goes to MXFP4 with the library's quantiser."""
+    import numpy as np
+
+    dev = torch.device("cuda", 0)
+    o_buf = torch.from_numpy(w.o_buf.view(np.int16)).view(torch.bfloat16).to(dev)
+    o = torch.as_strided(o_buf, (w.n, w.S, 12, 512), tuple(w.o_strides) + (1,))
+    lse = None
+    if w.lse_buf is not None:
+        lse = torch.as_strided(torch.from_numpy(w.lse_buf).to(dev), (w.n, w.S, 12), tuple(w.lse_strides))
+    wv = torch.from_numpy(w.wv_bits.reshape(-1, 512).view(np.int16)).view(torch.bfloat16).to(dev)
+    codes, scales = m.quantize_mxfp4(wv)
+    w_v = codes.view(12, 128, 256)
+    w_s = scales.view(12, 128, 16)
+    gate = torch.from_numpy(w.gate.view(np.int16)).view(torch.bfloat16).to(dev)
+    core = torch.empty((w.S, 1536), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    return dict(o=o, lse=lse, w_v=w_v, w_s=w_s, gate=gate, core=core, o_buf=o_buf)
+
+
+def time_gpu(call, steps: int, warmup: int, torch) -> dict:
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"wall_s": wall, "event_ms": ev0.elapsed_time(ev1)}
+
+
+def cpu_baseline(w, tokens: int) -> dict:
+    """The oracle as it is, single-threaded (BLAS limited to one thread), on
+    the first `tokens` tokens of the same workload; W_V encoded by the
+    oracle's own quantiser (not timed)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.post as O
+
+    codes, scales = O.quantize_mxfp4(w.wv_bits)
+    o, lse = w.o_view(), w.lse_view()
+    chunk = 64
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s0 in range(0, tokens, chunk):
+            O.mla_post(o, lse, codes, scales, w.gate, tokens=np.arange(s0, min(tokens, s0 + chunk)))
+        dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(tokens / dt, 2),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {tokens} of {w.S} tokens of the same workload, in chunks of {chunk}, one thread "
+        f"({dt:.1f} s; host {cpu}, {os.cpu_count()} logical CPUs)",
+    }
+
+
+def traffic_entry(alg: dict):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def counter_kib(csv_path: str, kernel_substr: str) -> list:
+    """Per-dispatch values (KiB) of the one counter in a rocprofv3 --pmc CSV,
+    for dispatches whose kernel name contains kernel_substr."""
+    import csv
+
+    with open(csv_path) as f:
+        return [float(r["Counter_Value"]) for r in csv.DictReader(f) if kernel_substr in r["Kernel_Name"]]
+
+
+def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str) -> dict:
+    """HBM bytes per launch of the fused kernel from FETCH_SIZE / WRITE_SIZE
+    runs, each scaled by what the same counter reads for the plain 1 GiB copy
+    (true bytes / counter bytes). Writes TRAFFIC_FILE."""
+    import statistics
+
+    copy_bytes = 1 << 30
+    fk = statistics.median(counter_kib(fetch_csv, "mla_post_kernel"))
+    wk = statistics.median(counter_kib(write_csv, "mla_post_kernel"))
+    cf = statistics.median(counter_kib(copy_fetch_csv, "copyBuffer"))
+    cw = statistics.median(counter_kib(copy_write_csv, "copyBuffer"))
+    f_scale = copy_bytes / (cf * 1024)
+    w_scale = copy_bytes / (cw * 1024)
+    fetch = fk * 1024 * f_scale
+    write = wk * 1024 * w_scale
+    out = {
+        "kernel": "mla_post_kernel<false, 1> (large decode workload)",
+        "kernel_source_sha256": kernel_sha(),
+        "fetch_kib_per_dispatch": fk,
+        "write_kib_per_dispatch": wk,
+        "copy_fetch_kib": cf,
+        "copy_write_kib": cw,
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "hbm_fetch_bytes": round(fetch),
+        "hbm_write_bytes": round(write),
+        "hbm_bytes_per_launch": round(fetch + write),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
+def calibrate_copy(torch) -> None:
+    """A plain device-to-device copy of 1 GiB (torch dispatches it to the HIP
+    runtime copy kernel __amd_rocclr_copyBuffer): counter
+    runs of this give the bytes-per-counter-unit factor."""
+    n = 1 << 29  # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": 2 * n}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time the four other standard workloads (stderr)")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument(
+        "--traffic-from",
+        nargs=4,
+        metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+        help="turn rocprofv3 --pmc counter CSVs into the committed traffic figure (no GPU needed)",
+    )
+    args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from(*args.traffic_from), indent=1))
+        return 0
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(
+            "bench.py measures one GPU only: the mla_post path has no multi-GPU stage in this build "
+            "(the decode-context-parallel exchange is not implemented); run with --gpus 1.",
+            file=sys.stderr,
+        )
+        return 2
+
+    import torch
+
+    import mla_split_kv_amd as m
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    m.load()
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return 0
+
+    log("generating the large decode workload (seeded, 805 MB of partials)")
+    w = synth.large_decode()
+    alg = algorithmic_bytes(w)
+    d = device_setup(w, m, torch)
+    call = m.prepare(d["o"], d["lse"], d["w_v"], d["w_s"], d["gate"], d["core"])
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    t = time_gpu(call, args.steps, args.warmup, torch)
+    ms_per_step = 1e3 * t["wall_s"] / args.steps
+    kernel_us = 1e3 * t["event_ms"] / args.steps
+    achieved = alg["alg_bytes"] / (kernel_us * 1e-6) / 1e9
+    tokens_per_s = w.S * args.steps / t["wall_s"]
+
+    extra = {}
+    if args.all:
+        for name in ("tiny", "no_merge", "split_merge", "dcp8"):
+            wk = synth.STANDARD[name]()
+            dk = device_setup(wk, m, torch)
+            ck = m.prepare(dk["o"], dk["lse"], dk["w_v"], dk["w_s"], dk["gate"], dk["core"])
+            tk = time_gpu(ck, 2000, 100, torch)
+            ak = algorithmic_bytes(wk)
+            us = 1e3 * tk["event_ms"] / 2000
+            extra[name] = {"us_per_call": round(us, 3), "GBps": round(ak["alg_bytes"] / (us * 1e-6) / 1e9, 1)}
+            log(f"{name}: {extra[name]}")
+            del dk, ck
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(w, args.cpu_tokens)
+
+    out = {
+        "metric": "tokens/s and us per mla_post call; achieved HBM GB/s vs peak (1 GPU)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_call": round(kernel_us, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "large_decode",
+            "tokens": w.S,
+            "splits": w.n,
+            "heads": 12,
+            "latent": 512,
+            "v_dim": 128,
+            "live_rows": alg["live_rows"],
+            "rows": alg["rows"],
+            "alg_bytes_per_call": alg["alg_bytes"],
+            "nominal_bytes_per_call": alg["nominal_bytes"],
+            "parallelism": "single GPU",
+            "compute": "fp32 merge of bf16 rows, MXFP4 x MXFP4 MFMA, bf16 out",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_entry(alg),
+        },
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        out["other_workloads"] = extra
+    log(f"host: {platform.node()} python {platform.python_version()} torch {torch.__version__}")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -216,6 +216,31 @@ def mla_post(o, lse, w_v, w_v_scale, gate, core=None, debug: bool = False):
     return core if not debug else (core,) + dbg
 
 
+class Prepared:
+    """A validated mla_post call whose argument struct is built once; calling
+    it enqueues the kernel on torch's current stream (for timing loops and
+    serving loops that reuse the same buffers)."""
+
+    def __init__(self, o, lse, w_v, w_v_scale, gate, core, dbg=None):
+        self._lib = load()
+        _need(core.is_cuda, ValueError, "tensors must be on a GPU")
+        self._keep = (o, lse, w_v, w_v_scale, gate, core, dbg)
+        self.args = make_args(o, lse, w_v, w_v_scale, gate, core, dbg)
+        self._ref = ctypes.byref(self.args)
+        self.device = core.device
+        _raise(self._lib, self._lib.mla_post_check(self._ref))
+
+    def __call__(self, stream: int | None = None):
+        s = _stream(self.device) if stream is None else stream
+        st = self._lib.mla_post(self._ref, ctypes.c_void_p(s))
+        if st:
+            _raise(self._lib, st)
+
+
+def prepare(o, lse, w_v, w_v_scale, gate, core):
+    return Prepared(o, lse, w_v, w_v_scale, gate, core)
+
+
 def mla_post_splits(o, lse, w_v, w_v_scale, gate, core=None, debug=False):
     """Split-KV partials: o [P, S, 12, 512], lse [P, S, 12] (token t merges o[:, t])."""
     return mla_post(o, lse, w_v, w_v_scale, gate, core, debug)
