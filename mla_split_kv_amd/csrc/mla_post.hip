@@ -40,6 +40,16 @@ constexpr int WAVES = VD / 16;                 // 8 waves x 16 W_V rows
 constexpr int THREADS = WAVES * 64;            // 512
 constexpr int TOK_PER_WAVE = TILE_T / WAVES;   // 2
 constexpr int ROWS_IN_FLIGHT = 8;              // partial rows a wave loads before it sums
+constexpr bool NT_ROWS = true;                 // partial rows loaded non-temporally
+constexpr bool LATE_WV = false;                // W_V operands loaded after the merge, not before
+// A token tile's 12 heads on one XCD (xcd_task): measured on the large decode
+// workload it removes the duplicate L2 fetches (HBM reads 804 -> 784 MB per
+// launch) but runs 2.5% slower (134.1 -> 137.4 us), so it is off.
+constexpr bool XCD_REMAP = false;
+constexpr int NXCD = 8;                        // XCDs of an MI355X
+#ifndef MLA_KERNEL_ATTRS
+#define MLA_KERNEL_ATTRS
+#endif
 constexpr int NBLK = KVL / 32;                 // 16 MXFP4 blocks per latent row
 constexpr int CODE_ROW = TILE_T * 16 + 16;     // LDS bytes per block row (+16 B skew)
 constexpr int LDS_CODES = NBLK * CODE_ROW;     // 4352 B
@@ -131,21 +141,27 @@ __device__ __forceinline__ v4f mfma_step(const uint4& a, const uint4& b, v4f acc
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, ST, sa, ST, sb);
 }
 
-// LSE weights of one (t, h): lane j of chunk c holds w_{64c + j}.
-// [mla_back: combine_splits] / [mla_back: combine_ranks]: m = max, 0 when all
-// are -inf; e = exp(lse - m); weight e / sum, 0 when e == 0 or the sum is 0.
+// Sanitised LSEs of one (t, h): lane j of chunk c holds lse_{64c + j}, -inf
+// past n ([mla_back: sane]).
 template <int NCH>
-__device__ __forceinline__ void lse_weights(const KArgs& a, int t, int h, int lane, float wts[NCH]) {
-  float l[NCH];
-  float m = -INFINITY;
+__device__ __forceinline__ void load_lse(const KArgs& a, int t, int h, int lane, float l[NCH]) {
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    int j = 64 * c + lane;
+    const int j = 64 * c + lane;
     float x = -INFINITY;
     if (j < a.n) x = sane(a.lse[(int64_t)j * a.l_sj + (int64_t)t * a.l_st + (int64_t)h * a.l_sh]);
     l[c] = x;
-    m = fmaxf(m, x);
   }
+}
+
+// LSEs -> merge weights, in place ([mla_back: combine_splits],
+// [mla_back: combine_ranks]): m = max, 0 when all are -inf; e = exp(lse - m);
+// weight e / sum, 0 when e == 0 or the sum is 0.
+template <int NCH>
+__device__ __forceinline__ void lse_to_weights(float l[NCH]) {
+  float m = l[0];
+#pragma unroll
+  for (int c = 1; c < NCH; ++c) m = fmaxf(m, l[c]);
   m = wave_max(m);
   if (m == -INFINITY) m = 0.f;
   float s = 0.f;
@@ -154,9 +170,21 @@ __device__ __forceinline__ void lse_weights(const KArgs& a, int t, int h, int la
     l[c] = expf(l[c] - m);
     s += l[c];
   }
-  float tot = wave_sum(s);
+  const float tot = wave_sum(s);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) wts[c] = (tot == 0.f || l[c] == 0.f) ? 0.f : l[c] / tot;
+  for (int c = 0; c < NCH; ++c) l[c] = (tot == 0.f || l[c] == 0.f) ? 0.f : l[c] / tot;
+}
+
+// One 1 KiB partial row: 16 B per lane. The rows are read once, so they are
+// loaded non-temporally and do not push W_V out of L2.
+__device__ __forceinline__ uint4 load_row16(const uint8_t* p, int lane) {
+  if constexpr (NT_ROWS) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + lane);
+    return make_uint4(t.x, t.y, t.z, t.w);
+  } else {
+    return reinterpret_cast<const uint4*>(p)[lane];
+  }
 }
 
 // Weighted sum of the partial rows of (t, h) for this lane's 8 latents
@@ -178,10 +206,7 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, const uint8_t* rowbas
         if (jl >= nc) wb = 0;
         wj[b] = __int_as_float(wb);
         v[b] = make_uint4(0, 0, 0, 0);
-        if (wb & 0x7FFFFFFF) {
-          const uint8_t* p = rowbase + (int64_t)(64 * c + jl) * a.o_sj;
-          v[b] = reinterpret_cast<const uint4*>(p)[lane];
-        }
+        if (wb & 0x7FFFFFFF) v[b] = load_row16(rowbase + (int64_t)(64 * c + jl) * a.o_sj, lane);
       }
 #pragma unroll
       for (int b = 0; b < ROWS_IN_FLIGHT; ++b) {
@@ -199,69 +224,102 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, const uint8_t* rowbas
   }
 }
 
+// W_V[h] rows wave*16 + tl, K block kb of each of the 4 K steps
+// ([mla_back: wv_loads]); the four scale bytes packed into one word, byte st
+// for K step st.
+__device__ __forceinline__ void load_wv(const KArgs& a, int h, int wave, int tl, int kb, uint4 wv[4], int& sa) {
+  const int v = wave * 16 + tl;
+  const uint8_t* wrow = a.w_v + h * a.w_sh + v * a.w_sv + kb * 16;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) wv[st] = *reinterpret_cast<const uint4*>(wrow + st * 64);
+  const uint8_t* srow = a.w_vs + h * a.s_sh + v * a.s_sv;
+  sa = 0;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) sa |= (int)srow[(st * 4 + kb) * a.s_sb] << (8 * st);
+}
+
+// Latents of token t (tile slot tt) -> bf16 -> MXFP4 codes and scale into
+// LDS (the MFMA B operand) and, if asked, the stage outputs.
+template <bool NOLSE, int NCH>
+__device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h, int lane, bool live,
+                                            const float wts[NCH], uint8_t* s_codes, uint8_t* s_scales) {
+  uint32_t lat[4] = {0u, 0u, 0u, 0u};
+  if (live) {
+    const uint8_t* rowbase = a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
+    if constexpr (NOLSE) {
+      // one partial and no LSE: the row is the attention output itself
+      const uint4 v = load_row16(rowbase, lane);
+      lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+    } else {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      merge_rows<NCH>(a, rowbase, lane, wts, acc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
+    }
+  }
+  int code;
+  const uint32_t pk = quant8(lat, code);
+  const int b = lane >> 2;  // this lane's block
+  *reinterpret_cast<uint32_t*>(s_codes + b * CODE_ROW + tt * 16 + (lane & 3) * 4) = live ? pk : 0u;
+  if ((lane & 3) == 0) s_scales[tt * NBLK + (b & 3) * 4 + (b >> 2)] = (uint8_t)code;
+  if (live) {
+    const int64_t th = (int64_t)t * NH + h;
+    if (a.dbg_lat)
+      reinterpret_cast<uint4*>(a.dbg_lat + th * (KVL * 2))[lane] = make_uint4(lat[0], lat[1], lat[2], lat[3]);
+    if (a.dbg_codes) reinterpret_cast<uint32_t*>(a.dbg_codes + th * (KVL / 2))[lane] = pk;
+    if (a.dbg_scales && (lane & 3) == 0) a.dbg_scales[th * NBLK + b] = (uint8_t)code;
+  }
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8),
+// and each XCD has its own L2. Task = (token tile, head), head-minor; the
+// remap gives each XCD a contiguous run of tasks, so the 12 heads of a token
+// tile run on one XCD at about the same time and share its L2 lines of LSEs
+// (12 heads interleaved every 48 B) and neighbouring partial rows. The
+// remainder of the grid past the last multiple of 8 maps to itself.
+__device__ __forceinline__ int xcd_task(int b, int nblocks) {
+  if constexpr (!XCD_REMAP) return b;
+  const int full = nblocks & ~(NXCD - 1);
+  if (b >= full) return b;
+  return (b % NXCD) * (full / NXCD) + b / NXCD;
+}
+
 // ---------------------------------------------------------------- the fused kernel
 
 template <bool NOLSE, int NCH>
-__global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a) {
+__global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.x % NH;
-  const int t0 = (blockIdx.x / NH) * TILE_T;
+  const int task = xcd_task(blockIdx.x, gridDim.x);
+  const int h = task % NH;
+  const int t0 = (task / NH) * TILE_T;
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
-  // W_V[h] rows wave*16 + tl, K block kb of each of the 4 K steps
-  // ([mla_back: wv_loads]): issued first, consumed after the merge.
   uint4 wv[4];
   int sa = 0;
-  {
-    const int v = wave * 16 + tl;
-    const uint8_t* wrow = a.w_v + h * a.w_sh + v * a.w_sv + kb * 16;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) wv[st] = *reinterpret_cast<const uint4*>(wrow + st * 64);
-    const uint8_t* srow = a.w_vs + h * a.s_sh + v * a.s_sv;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) sa |= (int)srow[(st * 4 + kb) * a.s_sb] << (8 * st);
-  }
+  if constexpr (!LATE_WV) load_wv(a, h, wave, tl, kb, wv, sa);
 
-  // ---- merge + quantise: wave owns tokens t0 + 2 wave, t0 + 2 wave + 1
-#pragma unroll 1
-  for (int i = 0; i < TOK_PER_WAVE; ++i) {
-    const int tt = wave * TOK_PER_WAVE + i;
-    const int t = t0 + tt;
-    uint32_t lat[4] = {0u, 0u, 0u, 0u};
-    const bool live = t < a.S;
-    if (live) {
-      const uint8_t* rowbase = a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
-      if constexpr (NOLSE) {
-        // one partial and no LSE: the row is the attention output itself
-        uint4 v = reinterpret_cast<const uint4*>(rowbase)[lane];
-        lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
-      } else {
-        float wts[NCH];
-        lse_weights<NCH>(a, t, h, lane, wts);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        merge_rows<NCH>(a, rowbase, lane, wts, acc);
+  // ---- merge + quantise: wave owns tile slots 2 wave and 2 wave + 1
+  const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
+  const int tA = t0 + ttA, tB = t0 + ttB;
+  const bool liveA = tA < a.S, liveB = tB < a.S;
+  float wA[NCH], wB[NCH];
+  if constexpr (!NOLSE) {
+    // both tokens' LSE loads in flight before either reduction
 #pragma unroll
-        for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
-      }
-    }
-    int code;
-    uint32_t pk = quant8(lat, code);
-    const int b = lane >> 2;  // this lane's block
-    *reinterpret_cast<uint32_t*>(s_codes + b * CODE_ROW + tt * 16 + (lane & 3) * 4) = live ? pk : 0u;
-    if ((lane & 3) == 0) s_scales[tt * NBLK + (b & 3) * 4 + (b >> 2)] = (uint8_t)code;
-    if (live) {
-      const int64_t th = (int64_t)t * NH + h;
-      if (a.dbg_lat)
-        reinterpret_cast<uint4*>(a.dbg_lat + th * (KVL * 2))[lane] = make_uint4(lat[0], lat[1], lat[2], lat[3]);
-      if (a.dbg_codes) reinterpret_cast<uint32_t*>(a.dbg_codes + th * (KVL / 2))[lane] = pk;
-      if (a.dbg_scales && (lane & 3) == 0) a.dbg_scales[th * NBLK + b] = (uint8_t)code;
-    }
+    for (int c = 0; c < NCH; ++c) wA[c] = wB[c] = -INFINITY;
+    if (liveA) load_lse<NCH>(a, tA, h, lane, wA);
+    if (liveB) load_lse<NCH>(a, tB, h, lane, wB);
+    if (liveA) lse_to_weights<NCH>(wA);
+    if (liveB) lse_to_weights<NCH>(wB);
   }
+  token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, wA, s_codes, s_scales);
+  token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, wB, s_codes, s_scales);
+  if constexpr (LATE_WV) load_wv(a, h, wave, tl, kb, wv, sa);
   __syncthreads();
 
   // ---- W_UV: D[v][token] = sum_k W_V[h][v][k] * L[token][k]
