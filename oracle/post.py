@@ -344,6 +344,53 @@ def gate_core(acc_bf, gate_bits) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Request-major split partials and push-side masking
+# --------------------------------------------------------------------------
+
+
+def gather_request_major(o_all, lse_all, q: int):
+    """The page's split layout ([mla_back: combine_splits]): the partials of
+    all requests sit in one dense tensor of P split slices, o_all
+    [P, S, 12, 512] and lse_all [P, S, 12], request-major; with R = S / q
+    requests of q tokens and per = P / R splits each, token t merges slices
+    (t // q) * per + j for j < per. Returns the per-token views o [per, S,
+    12, 512] and lse [per, S, 12] that ``mla_post`` takes.
+    """
+    P, S = o_all.shape[0], o_all.shape[1]
+    if S % q:
+        raise ValueError("S must be a whole number of requests")
+    R = S // q
+    if P % R:
+        raise ValueError("the split slices must divide evenly among the requests")
+    per = P // R
+    t = np.arange(S)
+    idx = (t // q)[None, :] * per + np.arange(per)[:, None]  # [per, S]
+    o = np.asarray(o_all)[idx, t[None, :]]
+    lse = np.asarray(lse_all)[idx, t[None, :]]
+    return o, lse
+
+
+def push_mask(lse, q: int, kv_lens=None, qsl=None):
+    """Push-side masking of partial LSEs ([mla_back: stage_push]): the partial
+    of token t is empty, its LSE -inf, when the request t // q has no KV in
+    that partial (kv_lens[j, t // q] == 0; kv_lens [n, R], one row per
+    partial) or when t lies past the batch (t >= qsl[S // q], qsl the R + 1
+    query start offsets). Returns a float64 copy of lse [n, S, 12].
+    """
+    v = np.asarray(lse, dtype=np.float64).copy()
+    n, S = v.shape[0], v.shape[1]
+    t = np.arange(S)
+    if kv_lens is not None:
+        kv = np.asarray(kv_lens).reshape(n, -1)
+        empty = kv[:, t // q] == 0  # [n, S]
+        v[empty] = -np.inf
+    if qsl is not None:
+        rows = int(np.asarray(qsl)[S // q])
+        v[:, t >= rows] = -np.inf
+    return v
+
+
+# --------------------------------------------------------------------------
 # The whole step
 # --------------------------------------------------------------------------
 
@@ -408,6 +455,8 @@ __all__ = [
     "dequant_mxfp4",
     "wuv_exact",
     "gate_core",
+    "gather_request_major",
+    "push_mask",
     "mla_post",
     "ulp_bf16",
 ]

@@ -581,6 +581,64 @@ def pin_end_to_end_small():
             assert np.mean(core == r["core"][t, 128 * h : 128 * h + 128]) > 0.99
 
 
+def pin_request_major_gather():
+    """The page's request-major split layout: token t takes slices
+    (t // q) * per + j, checked against explicit loops; with one request the
+    gather is the identity; slices of other requests (NaN-filled) are never
+    read by the merge."""
+    rng = np.random.default_rng(27)
+    for P, S, q in ((6, 6, 2), (8, 4, 4), (12, 12, 3), (5, 5, 5)):
+        R = S // q
+        per = P // R
+        o_all = rng.standard_normal((P, S, 2, 3))
+        l_all = rng.standard_normal((P, S, 2))
+        o, l = O.gather_request_major(o_all, l_all, q)
+        assert o.shape == (per, S, 2, 3) and l.shape == (per, S, 2)
+        for j in range(per):
+            for t in range(S):
+                assert np.array_equal(o[j, t], o_all[(t // q) * per + j, t])
+                assert np.array_equal(l[j, t], l_all[(t // q) * per + j, t])
+        if R == 1:
+            assert np.array_equal(o, o_all)
+    # foreign slices poisoned with NaN: the merged latents stay finite
+    P, S, q = 8, 8, 2
+    R, per = S // q, P // (S // q)
+    o_all = np.full((P, S, O.NH, O.KVL), 0x7FC0, dtype=np.uint16)
+    lse_all = np.full((P, S, O.NH), np.nan, dtype=np.float32)
+    vals = bf16_bits_from_f32(rng.standard_normal((per, S, O.NH, O.KVL)).astype(np.float32))
+    lv = rng.uniform(-2, 6, size=(per, S, O.NH)).astype(np.float32)
+    for t in range(S):
+        for j in range(per):
+            o_all[(t // q) * per + j, t] = vals[j, t]
+            lse_all[(t // q) * per + j, t] = lv[j, t]
+    o, l = O.gather_request_major(o_all, lse_all, q)
+    x, _ = O.merge(o, l)
+    x_ref, _ = O.merge(vals, lv)
+    assert np.array_equal(x, x_ref) and np.all(np.isfinite(x))
+
+
+def pin_push_mask():
+    """Push-side masking: a partial whose request has no KV there, or a token
+    past the batch, merges exactly as if its LSE were -inf; checked against
+    loops; tokens past the batch give +0 latents."""
+    rng = np.random.default_rng(28)
+    n, S, q = 3, 12, 4
+    R = S // q
+    o, lse = _dense_case(rng, n, S)
+    kv = rng.integers(0, 3, size=(n, R)).astype(np.int32)  # zeros mark requests without KV
+    qsl = np.array([0, 4, 8, 10], dtype=np.int32)  # 10 live tokens of 12
+    m = O.push_mask(lse, q, kv, qsl)
+    ref = lse.astype(np.float64).copy()
+    for j in range(n):
+        for t in range(S):
+            if kv[j, t // q] == 0 or t >= qsl[R]:
+                ref[j, t] = -np.inf
+    assert np.array_equal(m, ref)
+    x, _ = O.merge(o, m)
+    assert np.all(O.rne_bf16(x)[10:] == 0)
+    assert np.array_equal(O.push_mask(lse, q), lse.astype(np.float64))  # no masks: unchanged
+
+
 ALL_PINS = [
     pin_textbook_attention,
     pin_single_partial_identity,
@@ -601,4 +659,6 @@ ALL_PINS = [
     pin_wuv_one_hot,
     pin_gate_core,
     pin_end_to_end_small,
+    pin_request_major_gather,
+    pin_push_mask,
 ]

@@ -122,6 +122,26 @@ def _gate_transposed(acc_bf, gate_bits):
     return O.rne_bf16(a * O.bf16_to_f64(gate_bits).reshape(T, -1))
 
 
+def _gather_shifted(o_all, lse_all, q):
+    P, S = o_all.shape[0], o_all.shape[1]
+    per = P // (S // q)
+    t = np.arange(S)
+    idx = np.minimum(((t + 1) // q)[None, :] * per + np.arange(per)[:, None], P - 1)
+    return np.asarray(o_all)[idx, t[None, :]], np.asarray(lse_all)[idx, t[None, :]]
+
+
+def _push_mask_token_index(lse, q, kv_lens=None, qsl=None):
+    v = np.asarray(lse, dtype=np.float64).copy()
+    n, S = v.shape[0], v.shape[1]
+    t = np.arange(S)
+    if kv_lens is not None:
+        kv = np.asarray(kv_lens).reshape(n, -1)
+        v[kv[:, np.minimum(t, kv.shape[1] - 1)] == 0] = -np.inf  # request index taken as t
+    if qsl is not None:
+        v[:, t >= int(np.asarray(qsl)[S // q])] = -np.inf
+    return v
+
+
 MUTATIONS = [
     ("sanitize misses +inf", "sanitize_lse", _sanitize_no_posinf, [pins.pin_nan_inf_as_neg_inf]),
     ("sanitize misses NaN", "sanitize_lse", _sanitize_no_nan, [pins.pin_nan_inf_as_neg_inf]),
@@ -139,6 +159,8 @@ MUTATIONS = [
     ("scale bias off by one", "wuv_exact", _wuv_bias_off, [pins.pin_wuv_one_hot]),
     ("W_V rows reversed", "wuv_exact", _wuv_rows_reversed, [pins.pin_wuv_one_hot]),
     ("gate columns transposed", "gate_core", _gate_transposed, [pins.pin_gate_core]),
+    ("request index off by one", "gather_request_major", _gather_shifted, [pins.pin_request_major_gather]),
+    ("mask uses token not request", "push_mask", _push_mask_token_index, [pins.pin_push_mask]),
 ]
 
 
