@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MLA_POST_VERSION 1
+#define MLA_POST_VERSION 2
 
 /* Fixed shapes (the page's per-rank Kimi-K3 shapes at 8-way tensor parallelism). */
 #define MLA_POST_HEADS 12   /* local heads */
@@ -68,7 +68,7 @@ extern "C" {
  *   - one partial, no LSE (n == 1, lse == NULL): o [S, 12, 512].
  */
 typedef struct mla_post_args {
-  uint32_t struct_size; /* sizeof(mla_post_args) */
+  uint32_t struct_size; /* sizeof(mla_post_args), or MLA_POST_ARGS_V1_SIZE */
   int32_t n;            /* partials per (token, head): splits or ranks, 1..MLA_POST_NMAX */
   int32_t S;            /* tokens; 0 is a no-op */
   int32_t reserved;
@@ -99,7 +99,27 @@ typedef struct mla_post_args {
   void* dbg_lat;
   void* dbg_codes;
   void* dbg_scales;
+
+  /* ---- since version 2; a caller whose struct_size ends above leaves them off.
+   * Request-major split slices and push-side masking (the page's
+   * combine_splits addressing and stage_push masking). With R = S / q requests
+   * of q consecutive tokens, token t belongs to request r = t / q:
+   *   row (j, t, h) = o + j*o_sj + r*o_sr + t*o_st + h*o_sh,
+   *   LSE (j, t, h) = lse + j*l_sj + r*l_sr + t*l_st + h*l_sh.
+   * The page's dense layout of per = P / R slices per request in one tensor
+   * [P, S, 12, 512] is (o_sj, o_sr, o_st) = (S*6144, per*S*6144, 6144) with
+   * n = per. Partial j of token t is empty (LSE taken as -inf, row not read)
+   * when kv_lens[j*kl_sj + r] == 0, or for every j when t >= qsl[R]. */
+  int32_t q;              /* tokens per request; 0 or 1 = one token each. S % q == 0 */
+  int32_t reserved2;
+  int64_t o_sr, l_sr;     /* elements per request index, >= 0; o_sr a multiple of 8 */
+  const int32_t* kv_lens; /* NULL, or int32 KV lengths, entry (j, r) at j*kl_sj + r; 4-byte aligned */
+  int64_t kl_sj;          /* >= 0; 0 shares one row of R lengths among all partials */
+  const int32_t* qsl;     /* NULL, or int32 [R + 1] query start offsets; tokens >= qsl[R] are past the batch */
 } mla_post_args;
+
+/* Size of the version-1 prefix of mla_post_args (fields up to dbg_scales). */
+#define MLA_POST_ARGS_V1_SIZE 176
 
 /* Validate and enqueue one mla_post call on `stream` (a hipStream_t; NULL is
  * the default stream). Returns MLA_POST_OK or a negative status. */

@@ -62,7 +62,17 @@ class MlaPostArgs(ctypes.Structure):
         ("dbg_lat", ctypes.c_void_p),
         ("dbg_codes", ctypes.c_void_p),
         ("dbg_scales", ctypes.c_void_p),
+        ("q", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+        ("o_sr", ctypes.c_int64),
+        ("l_sr", ctypes.c_int64),
+        ("kv_lens", ctypes.c_void_p),
+        ("kl_sj", ctypes.c_int64),
+        ("qsl", ctypes.c_void_p),
     ]
+
+
+ARGS_V1_SIZE = 176  # MLA_POST_ARGS_V1_SIZE: the struct up to dbg_scales
 
 
 EXPORTS = (
@@ -134,7 +144,7 @@ def _need(cond: bool, exc, msg: str):
         raise exc(msg)
 
 
-def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None) -> MlaPostArgs:
+def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None, q=1, o_sr=0, l_sr=0, kv_lens=None, qsl=None) -> MlaPostArgs:
     """Validate tensors (the checks of the page's host_args) and fill the struct.
 
     o      bf16 [n, S, 12, 512] view, innermost stride 1 (any other strides)
@@ -144,6 +154,11 @@ def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None) -> MlaPostArgs:
     w_v_scale uint8 [12, 128, 16] E8M0 codes, any strides
     gate, core  bf16 [S, 1536], contiguous
     dbg    optional (lat bf16 [S,12,512], codes u8 [S,12,256], scales u8 [S,12,16])
+    q, o_sr, l_sr  request-major slices: token t of request t // q reads row
+           o[j, t, h] + (t // q) * o_sr elements (and likewise lse with l_sr)
+    kv_lens  optional int32 [n, S // q] (or [S // q], shared): 0 marks the
+           partial of that request empty (the page's stage_push masking)
+    qsl    optional int32 [S // q + 1]: tokens >= qsl[S // q] are past the batch
     """
     _need(o.dim() == 4 and o.shape[2:] == (NH, KVL), ValueError, f"o must be [n, S, 12, 512], got {tuple(o.shape)}")
     n, S = int(o.shape[0]), int(o.shape[1])
@@ -182,6 +197,22 @@ def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None) -> MlaPostArgs:
     a.s_sh, a.s_sv, a.s_sb = w_v_scale.stride(0), w_v_scale.stride(1), w_v_scale.stride(2)
     a.gate = gate.data_ptr()
     a.core = core.data_ptr()
+    _need(q >= 1 and S % q == 0, ValueError, f"S={S} must be a multiple of q={q}")
+    a.q, a.o_sr, a.l_sr = q, o_sr, l_sr
+    R = S // q
+    if kv_lens is not None:
+        _need(kv_lens.dtype == torch.int32 and kv_lens.device == dev, TypeError, "kv_lens must be int32 on the device")
+        if kv_lens.dim() == 1:
+            _need(kv_lens.shape[0] == R and kv_lens.stride(0) == 1, ValueError, "kv_lens must be [S // q]")
+            a.kl_sj = 0
+        else:
+            _need(tuple(kv_lens.shape) == (n, R) and kv_lens.stride(1) == 1, ValueError, f"kv_lens must be [{n}, {R}]")
+            a.kl_sj = kv_lens.stride(0)
+        a.kv_lens = kv_lens.data_ptr()
+    if qsl is not None:
+        _need(qsl.dtype == torch.int32 and qsl.device == dev, TypeError, "qsl must be int32 on the device")
+        _need(tuple(qsl.shape) == (R + 1,) and qsl.is_contiguous(), ValueError, f"qsl must be [{R + 1}]")
+        a.qsl = qsl.data_ptr()
     if dbg is not None:
         lat, codes, scales = dbg
         _need(lat.dtype == torch.bfloat16 and tuple(lat.shape) == (S, NH, KVL) and lat.is_contiguous(), ValueError, "dbg lat")
@@ -191,12 +222,13 @@ def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None) -> MlaPostArgs:
     return a
 
 
-def mla_post(o, lse, w_v, w_v_scale, gate, core=None, debug: bool = False):
+def mla_post(o, lse, w_v, w_v_scale, gate, core=None, debug: bool = False, **layout):
     """One mla_post call on torch's current stream of core's device.
 
     Returns core (bf16 [S, 1536]); with ``debug=True`` returns
     (core, latents bf16 [S,12,512], codes u8 [S,12,256], scales u8 [S,12,16]),
-    all written by the same kernel launch.
+    all written by the same kernel launch. ``layout`` takes the request-major
+    and masking arguments of make_args (q, o_sr, l_sr, kv_lens, qsl).
     """
     lib = load()
     S = int(o.shape[1])
@@ -210,7 +242,7 @@ def mla_post(o, lse, w_v, w_v_scale, gate, core=None, debug: bool = False):
             torch.empty((S, NH, KVL // 2), dtype=torch.uint8, device=dev),
             torch.empty((S, NH, KVL // 32), dtype=torch.uint8, device=dev),
         )
-    a = make_args(o, lse, w_v, w_v_scale, gate, core, dbg)
+    a = make_args(o, lse, w_v, w_v_scale, gate, core, dbg, **layout)
     _need(core.is_cuda, ValueError, "tensors must be on a GPU")
     _raise(lib, lib.mla_post(ctypes.byref(a), ctypes.c_void_p(_stream(core.device))))
     return core if not debug else (core,) + dbg
@@ -244,6 +276,26 @@ def prepare(o, lse, w_v, w_v_scale, gate, core):
 def mla_post_splits(o, lse, w_v, w_v_scale, gate, core=None, debug=False):
     """Split-KV partials: o [P, S, 12, 512], lse [P, S, 12] (token t merges o[:, t])."""
     return mla_post(o, lse, w_v, w_v_scale, gate, core, debug)
+
+
+def request_major_layout(o_all, lse_all, q: int):
+    """The page's dense split layout: o_all [P, S, 12, 512], lse_all [P, S, 12]
+    with per = P / (S / q) slices for each request of q tokens, request-major;
+    token t merges slices (t // q) * per + j. Returns (o view [per, S, 12, 512],
+    lse view [per, S, 12], layout kwargs for mla_post)."""
+    P, S = int(o_all.shape[0]), int(o_all.shape[1])
+    _need(q >= 1 and S % q == 0 and P % (S // q) == 0, ValueError, "P and S must split evenly into S // q requests")
+    per = P // (S // q)
+    so, sl = o_all.stride(), lse_all.stride()
+    ov = o_all.as_strided((per, S, NH, KVL), so, o_all.storage_offset())
+    lv = lse_all.as_strided((per, S, NH), sl, lse_all.storage_offset())
+    return ov, lv, {"q": q, "o_sr": per * so[0], "l_sr": per * sl[0]}
+
+
+def mla_post_request_major(o_all, lse_all, q: int, w_v, w_v_scale, gate, core=None, debug=False, kv_lens=None, qsl=None):
+    """Split partials in the page's request-major layout (see request_major_layout)."""
+    ov, lv, lay = request_major_layout(o_all, lse_all, q)
+    return mla_post(ov, lv, w_v, w_v_scale, gate, core, debug, kv_lens=kv_lens, qsl=qsl, **lay)
 
 
 def ranks_view(o_gathered, lse_gathered, ranks: int):

@@ -25,6 +25,8 @@
 
 #include <stdint.h>
 
+#include <string.h>
+
 #include <string>
 
 #include "mla_post.h"
@@ -74,6 +76,12 @@ struct KArgs {
   uint8_t* dbg_codes;
   uint8_t* dbg_scales;
   int32_t n, S;
+  int32_t q;                // tokens per request, >= 1
+  int64_t o_sr;             // bytes per request index
+  int64_t l_sr;             // elements per request index
+  const int32_t* kv_lens;   // NULL or (j, r) at j * kl_sj + r
+  int64_t kl_sj;
+  const int32_t* qsl;       // NULL or [S / q + 1]
 };
 
 // ---------------------------------------------------------------- helpers
@@ -143,13 +151,18 @@ __device__ __forceinline__ v4f mfma_step(const uint4& a, const uint4& b, v4f acc
 
 // Sanitised LSEs of one (t, h): lane j of chunk c holds lse_{64c + j}, -inf
 // past n ([mla_back: sane]).
+// Push-side masking ([mla_back: stage_push]): a partial whose request r has
+// no KV in it (kv_lens[j, r] == 0) counts as LSE -inf.
 template <int NCH>
-__device__ __forceinline__ void load_lse(const KArgs& a, int t, int h, int lane, float l[NCH]) {
+__device__ __forceinline__ void load_lse(const KArgs& a, int t, int r, int h, int lane, float l[NCH]) {
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int j = 64 * c + lane;
     float x = -INFINITY;
-    if (j < a.n) x = sane(a.lse[(int64_t)j * a.l_sj + (int64_t)t * a.l_st + (int64_t)h * a.l_sh]);
+    if (j < a.n) {
+      x = sane(a.lse[(int64_t)j * a.l_sj + (int64_t)r * a.l_sr + (int64_t)t * a.l_st + (int64_t)h * a.l_sh]);
+      if (a.kv_lens && a.kv_lens[(int64_t)j * a.kl_sj + r] == 0) x = -INFINITY;
+    }
     l[c] = x;
   }
 }
@@ -240,16 +253,22 @@ __device__ __forceinline__ void load_wv(const KArgs& a, int h, int wave, int tl,
 
 // Latents of token t (tile slot tt) -> bf16 -> MXFP4 codes and scale into
 // LDS (the MFMA B operand) and, if asked, the stage outputs.
+// `empty`: every partial of token t is masked (past the batch), so the
+// latents are +0 without reading anything.
 template <bool NOLSE, int NCH>
-__device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h, int lane, bool live,
+__device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
                                             const float wts[NCH], uint8_t* s_codes, uint8_t* s_scales) {
   uint32_t lat[4] = {0u, 0u, 0u, 0u};
-  if (live) {
-    const uint8_t* rowbase = a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
+  if (live && !empty) {
+    const int r = t / a.q;
+    const uint8_t* rowbase = a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (int64_t)r * a.o_sr;
     if constexpr (NOLSE) {
       // one partial and no LSE: the row is the attention output itself
-      const uint4 v = load_row16(rowbase, lane);
-      lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+      // (unless its request is masked as having no KV)
+      if (!(a.kv_lens && a.kv_lens[r] == 0)) {
+        const uint4 v = load_row16(rowbase, lane);
+        lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+      }
     } else {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       merge_rows<NCH>(a, rowbase, lane, wts, acc);
@@ -307,18 +326,21 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
   const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
   const int tA = t0 + ttA, tB = t0 + ttB;
   const bool liveA = tA < a.S, liveB = tB < a.S;
+  // tokens at or past qsl[R] lie past the batch: every partial is empty
+  const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
+  const bool emptyA = tA >= batch_end, emptyB = tB >= batch_end;
   float wA[NCH], wB[NCH];
   if constexpr (!NOLSE) {
     // both tokens' LSE loads in flight before either reduction
 #pragma unroll
     for (int c = 0; c < NCH; ++c) wA[c] = wB[c] = -INFINITY;
-    if (liveA) load_lse<NCH>(a, tA, h, lane, wA);
-    if (liveB) load_lse<NCH>(a, tB, h, lane, wB);
-    if (liveA) lse_to_weights<NCH>(wA);
-    if (liveB) lse_to_weights<NCH>(wB);
+    if (liveA && !emptyA) load_lse<NCH>(a, tA, tA / a.q, h, lane, wA);
+    if (liveB && !emptyB) load_lse<NCH>(a, tB, tB / a.q, h, lane, wB);
+    if (liveA && !emptyA) lse_to_weights<NCH>(wA);
+    if (liveB && !emptyB) lse_to_weights<NCH>(wB);
   }
-  token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, wA, s_codes, s_scales);
-  token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, wB, s_codes, s_scales);
+  token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, emptyA, wA, s_codes, s_scales);
+  token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, emptyB, wB, s_codes, s_scales);
   if constexpr (LATE_WV) load_wv(a, h, wave, tl, kb, wv, sa);
   __syncthreads();
 
@@ -394,9 +416,33 @@ bool span_ok(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t
 
 bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
 
-int check_args(const mla_post_args* a) {
-  if (!a || a->struct_size < sizeof(mla_post_args)) return MLA_POST_EINVAL;
-  if (a->n < 1 || a->S < 0) return MLA_POST_EINVAL;
+// Copy the caller's arguments into the current layout: a version-1 caller's
+// struct ends after dbg_scales, and the later fields read as zero (off).
+int normalize(const mla_post_args* in, mla_post_args* out) {
+  if (!in || in->struct_size < MLA_POST_ARGS_V1_SIZE) return MLA_POST_EINVAL;
+  memset(out, 0, sizeof(*out));
+  memcpy(out, in, in->struct_size < sizeof(*out) ? in->struct_size : sizeof(*out));
+  out->struct_size = sizeof(*out);
+  return MLA_POST_OK;
+}
+
+// largest byte offset of a 4-index span: sum_i (n_i - 1) * s_i + tail fits int64
+bool span4_ok(const int64_t n[4], const int64_t s[4], int64_t tail) {
+  int64_t acc = tail;
+  for (int i = 0; i < 4; ++i) {
+    int64_t term;
+    if (n[i] < 1) continue;
+    if (!mul_ok(n[i] - 1, s[i], &term) || !add_ok(acc, term, &acc)) return false;
+  }
+  return true;
+}
+
+int check_args(const mla_post_args* in) {
+  mla_post_args na;
+  const int st = normalize(in, &na);
+  if (st != MLA_POST_OK) return st;
+  const mla_post_args* a = &na;
+  if (a->n < 1 || a->S < 0 || a->q < 0) return MLA_POST_EINVAL;
   if (a->n > MLA_POST_NMAX) return MLA_POST_EUNSUPPORTED;
   if (a->S == 0) return MLA_POST_OK;
   if (!a->o || !a->w_v || !a->w_v_scale || !a->gate || !a->core) return MLA_POST_EINVAL;
@@ -410,14 +456,25 @@ int check_args(const mla_post_args* a) {
     return MLA_POST_EALIGN;
   if (a->lse && !aligned(a->lse, 4)) return MLA_POST_EALIGN;
   if ((a->dbg_lat && !aligned(a->dbg_lat, 16)) || (a->dbg_codes && !aligned(a->dbg_codes, 4))) return MLA_POST_EALIGN;
+  const int q = a->q > 1 ? a->q : 1;
+  if (a->S % q) return MLA_POST_EINVAL;
+  const int64_t R = a->S / q;
+  if (a->o_sr < 0 || a->l_sr < 0 || (a->o_sr % 8) || a->kl_sj < 0) return MLA_POST_ESTRIDE;
+  if ((a->kv_lens && !aligned(a->kv_lens, 4)) || (a->qsl && !aligned(a->qsl, 4))) return MLA_POST_EALIGN;
   // every byte offset the kernel forms must fit int64
-  int64_t bsj, bst, bsh;
-  if (!mul_ok(a->o_sj, 2, &bsj) || !mul_ok(a->o_st, 2, &bst) || !mul_ok(a->o_sh, 2, &bsh) ||
-      !span_ok(a->n, bsj, a->S, bst, NH, bsh, KVL * 2))
-    return MLA_POST_ERANGE;
-  if (a->lse && (!mul_ok(a->l_sj, 4, &bsj) || !mul_ok(a->l_st, 4, &bst) || !mul_ok(a->l_sh, 4, &bsh) ||
-                 !span_ok(a->n, bsj, a->S, bst, NH, bsh, 4)))
-    return MLA_POST_ERANGE;
+  {
+    const int64_t n4[4] = {a->n, R, a->S, NH};
+    int64_t b4[4];
+    if (!mul_ok(a->o_sj, 2, &b4[0]) || !mul_ok(a->o_sr, 2, &b4[1]) || !mul_ok(a->o_st, 2, &b4[2]) ||
+        !mul_ok(a->o_sh, 2, &b4[3]) || !span4_ok(n4, b4, KVL * 2))
+      return MLA_POST_ERANGE;
+    if (a->lse && (!mul_ok(a->l_sj, 4, &b4[0]) || !mul_ok(a->l_sr, 4, &b4[1]) || !mul_ok(a->l_st, 4, &b4[2]) ||
+                   !mul_ok(a->l_sh, 4, &b4[3]) || !span4_ok(n4, b4, 4)))
+      return MLA_POST_ERANGE;
+    const int64_t nk[4] = {a->n, R, 1, 1};
+    int64_t bk[4] = {0, 4, 0, 0};
+    if (a->kv_lens && (!mul_ok(a->kl_sj, 4, &bk[0]) || !span4_ok(nk, bk, 4))) return MLA_POST_ERANGE;
+  }
   if (!span_ok(NH, a->w_sh, VD, a->w_sv, 1, 0, KVL / 2)) return MLA_POST_ERANGE;
   if (!span_ok(NH, a->s_sh, VD, a->s_sv, NBLK, a->s_sb, 1)) return MLA_POST_ERANGE;
   if (!span_ok(a->S, (int64_t)GROWS * 2, 1, 0, 1, 0, GROWS * 2)) return MLA_POST_ERANGE;
@@ -442,9 +499,12 @@ extern "C" {
 
 int mla_post_check(const mla_post_args* a) { return check_args(a); }
 
-int mla_post(const mla_post_args* a, void* stream) {
-  const int st = check_args(a);
-  if (st != MLA_POST_OK || a->S == 0) return st;
+int mla_post(const mla_post_args* in, void* stream) {
+  const int st = check_args(in);
+  if (st != MLA_POST_OK || in->S == 0) return st;
+  mla_post_args na;
+  normalize(in, &na);
+  const mla_post_args* a = &na;
   KArgs k;
   k.o = static_cast<const uint8_t*>(a->o);
   k.o_sj = a->o_sj * 2;
@@ -468,6 +528,12 @@ int mla_post(const mla_post_args* a, void* stream) {
   k.dbg_scales = static_cast<uint8_t*>(a->dbg_scales);
   k.n = a->n;
   k.S = a->S;
+  k.q = a->q > 1 ? a->q : 1;
+  k.o_sr = a->o_sr * 2;
+  k.l_sr = a->l_sr;
+  k.kv_lens = a->kv_lens;
+  k.kl_sj = a->kl_sj;
+  k.qsl = a->qsl;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!a->lse) return launch<true, 1>(k, a->S, s);
   if (a->n <= 64) return launch<false, 1>(k, a->S, s);

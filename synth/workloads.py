@@ -64,6 +64,12 @@ class Workload:
     gate: np.ndarray  # uint16 [S, 1536]
     seed: int = 0
     notes: dict = field(default_factory=dict)
+    # request-major slices: row (j, t, h) also moves by (t // q) * o_sr elements
+    q: int = 1
+    o_sr: int = 0
+    l_sr: int = 0
+    kv_lens: np.ndarray | None = None  # int32 [n, S // q]: 0 marks an empty partial
+    qsl: np.ndarray | None = None  # int32 [S // q + 1]
 
     def o_view(self) -> np.ndarray:
         """[N, S, 12, 512] numpy view into o_buf."""
@@ -191,6 +197,73 @@ def dcp_gathered(
         gate,
         seed,
     )
+
+
+def request_major(
+    name: str,
+    per: int,
+    q: int,
+    S: int,
+    seed: int,
+    compact: bool = False,
+    p_neg_inf: float = 0.1,
+    kv_zero: float = 0.0,
+    batch_rows: int | None = None,
+) -> Workload:
+    """Split partials laid out request-major, R = S / q requests of q tokens,
+    per splits each.
+
+    compact=False: the page's layout, one dense tensor of P = per * R slices,
+    o [P, S, 12, 512] and lse [P, S, 12]; token t's splits are slices
+    (t // q) * per + j. Only those (slice, token) rows are filled; every other
+    row is NaN and every other LSE NaN (never to be read).
+    compact=True: o [R, per, q, 12, 512], lse [R, per, q, 12]: no unused rows.
+
+    kv_zero: fraction of (partial, request) pairs whose KV length is 0
+    (kv_lens [per, R], otherwise lengths 1..64); batch_rows: qsl[R] (tokens
+    from there on are past the batch; qsl evenly spaced otherwise).
+    """
+    assert S % q == 0
+    R = S // q
+    rng = np.random.Generator(np.random.PCG64(seed))
+    vals = _normal_bf16(rng, (per, S, NH, KVL), 1.0)
+    lv = rng.uniform(-4.0, 16.0, size=(per, S, NH)).astype(np.float32)
+    u = rng.random((per, S, NH))
+    lv[u < p_neg_inf] = -np.inf
+    kv = rng.integers(1, 65, size=(per, R)).astype(np.int32)
+    kv[rng.random((per, R)) < kv_zero] = 0
+    qsl = (np.arange(R + 1, dtype=np.int32) * q).astype(np.int32)
+    if batch_rows is not None:
+        qsl[R] = batch_rows
+    wv, gate = _wv_gate(rng, S)
+    t = np.arange(S)
+    if compact:
+        o = np.empty((R, per, q, NH, KVL), dtype=np.uint16)
+        lse = np.empty((R, per, q, NH), dtype=np.float32)
+        for j in range(per):
+            o[t // q, j, t % q] = vals[j]
+            lse[t // q, j, t % q] = lv[j]
+        o_strides = (q * NH * KVL, NH * KVL, KVL)
+        o_sr = (per - 1) * q * NH * KVL
+        l_strides = (q * NH, NH, 1)
+        l_sr = (per - 1) * q * NH
+    else:
+        P = per * R
+        o = np.full((P, S, NH, KVL), NAN_BF16, dtype=np.uint16)
+        lse = np.full((P, S, NH), np.nan, dtype=np.float32)
+        for j in range(per):
+            o[(t // q) * per + j, t] = vals[j]
+            lse[(t // q) * per + j, t] = lv[j]
+        o_strides = (S * NH * KVL, NH * KVL, KVL)
+        o_sr = per * S * NH * KVL
+        l_strides = (S * NH, NH, 1)
+        l_sr = per * S * NH
+    w = Workload(name, per, S, o, o_strides, lse, l_strides, wv, gate, seed)
+    w.q, w.o_sr, w.l_sr = q, o_sr, l_sr
+    w.notes["o_logical"], w.notes["lse_logical"] = vals, lv  # what token t's split j holds
+    w.kv_lens = kv if kv_zero > 0 else None
+    w.qsl = qsl if batch_rows is not None else None
+    return w
 
 
 # ---- the five standard workloads -------------------------------------------

@@ -38,12 +38,27 @@ def device_inputs(w, dev="cuda", w_codes=None, w_scales=None) -> dict:
         "gate": bf16_to_dev(w.gate, dev),
         "w_codes": w_codes,
         "w_scales": w_scales,
+        "layout": layout_kwargs(w, dev),
     }
+
+
+def layout_kwargs(w, dev="cuda") -> dict:
+    """Request-major and masking arguments of workload w for the binding."""
+    kw = {}
+    if w.q != 1 or w.o_sr or w.l_sr:
+        kw.update(q=w.q, o_sr=w.o_sr, l_sr=w.l_sr)
+    if w.kv_lens is not None:
+        kw["kv_lens"] = torch.from_numpy(np.ascontiguousarray(w.kv_lens)).to(dev)
+    if w.qsl is not None:
+        kw["qsl"] = torch.from_numpy(np.ascontiguousarray(w.qsl)).to(dev)
+    return kw
 
 
 def run_debug(m, d) -> dict:
     """One launch with stage outputs; results as host arrays."""
-    core, lat, codes, scales = m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], debug=True)
+    core, lat, codes, scales = m.mla_post(
+        d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], debug=True, **d.get("layout", {})
+    )
     torch.cuda.synchronize()
     return {
         "core": to_bits(core),

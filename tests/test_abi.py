@@ -45,11 +45,12 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.mla_post_version() == 1
+    assert lib.mla_post_version() == 2
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.mla_post_strerror(st).decode()
     assert lib.mla_post_strerror(-99).decode() == "unknown status"
-    assert ctypes.sizeof(m.MlaPostArgs) == 4 * 4 + 8 * 20
+    assert ctypes.sizeof(m.MlaPostArgs) == 224
+    assert m.MlaPostArgs.q.offset == m.ARGS_V1_SIZE == 176
 
 
 def good_args(n=4, S=8):
@@ -122,6 +123,51 @@ def test_invalid_args_rejected(lib, field, value, status):
     assert check(lib, a) == status
     # mla_post validates first and returns the same status without launching
     assert lib.mla_post(ctypes.byref(a), None) == status
+
+
+@pytest.mark.parametrize(
+    "fields,status",
+    [
+        ({"q": -1}, EINVAL),
+        ({"q": 3}, EINVAL),  # S = 8 is not a multiple of 3
+        ({"q": 4, "o_sr": 4}, ESTRIDE),
+        ({"q": 4, "o_sr": -8}, ESTRIDE),
+        ({"q": 4, "l_sr": -1}, ESTRIDE),
+        ({"q": 2, "kv_lens": 0x800002}, EALIGN),
+        ({"qsl": 0x900001}, EALIGN),
+        ({"kv_lens": 0x800000, "kl_sj": -1}, ESTRIDE),
+        ({"q": 2, "o_sr": 1 << 61}, ERANGE),
+        ({"q": 2, "l_sr": 1 << 61}, ERANGE),
+        ({"kv_lens": 0x800000, "kl_sj": 1 << 62}, ERANGE),
+    ],
+)
+def test_request_major_args_rejected(lib, fields, status):
+    a = good_args()
+    for k, v in fields.items():
+        setattr(a, k, v)
+    assert check(lib, a) == status
+
+
+def test_request_major_args_accepted(lib):
+    a = good_args(n=4, S=8)
+    a.q, a.o_sr, a.l_sr = 4, 4 * 8 * 6144, 4 * 8 * 12
+    a.kv_lens, a.kl_sj, a.qsl = 0x800000, 2, 0x900000
+    assert check(lib, a) == OK
+    a.q = 0  # 0 means one token per request
+    assert check(lib, a) == OK
+
+
+def test_version1_struct_ignores_later_fields(lib):
+    """A version-1 caller (struct_size 176): fields past the prefix are not
+    read, so junk there passes; the same junk in a full-size struct fails."""
+    a = good_args()
+    a.q, a.o_sr, a.kv_lens = 7, 3, 0x11
+    a.struct_size = m.ARGS_V1_SIZE
+    assert check(lib, a) == OK
+    a.struct_size = ctypes.sizeof(m.MlaPostArgs)
+    assert check(lib, a) != OK
+    a.struct_size = m.ARGS_V1_SIZE - 8
+    assert check(lib, a) == EINVAL
 
 
 def test_debug_pointer_alignment(lib):

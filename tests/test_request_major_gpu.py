@@ -1,0 +1,147 @@
+"""Request-major split slices and push-side masking on the GPU, against the
+oracle (the mla_back page's combine_splits addressing and stage_push
+masking). All through the C ABI."""
+
+from __future__ import annotations
+
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import criteria as C
+import oracle.post as O
+import synth
+from gpu_support import device_inputs, run_debug, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def reference(w, d):
+    """Oracle inputs for w: the logical per-token partials (what split j of
+    token t holds) with the push-side masks applied to the LSEs."""
+    o_log, l_log = w.notes["o_logical"], w.notes["lse_logical"]
+    lse = O.push_mask(l_log, w.q, w.kv_lens, w.qsl)
+    return O.mla_post(o_log, lse, d["w_codes"], d["w_scales"], w.gate)
+
+
+def check(m, w):
+    say(f"{w.name}: per={w.n} q={w.q} S={w.S} o_sr={w.o_sr} masks={w.kv_lens is not None, w.qsl is not None}")
+    d = device_inputs(w)
+    g = run_debug(m, d)
+    ref = reference(w, d)
+    st = {}
+    st.update(C.check_t1(g["lat"], ref))
+    st.update(C.check_t2(g["lat"], g["codes"], g["scales"]))
+    st.update(C.check_t3(g["core"], g["codes"], g["scales"], d["w_codes"], d["w_scales"], w.gate))
+    st.update(C.check_t4(g["core"], ref, g["lat"], g["codes"], g["scales"]))
+    say(f"{w.name}: {st}")
+    return g, ref, d
+
+
+def test_page_dense_layout(gpu_lib):
+    """The page's layout: one [P, S, 12, 512] tensor of split slices, token t
+    merging slices (t // q) * per + j; every other row is NaN."""
+    w = synth.request_major("rm_page", per=4, q=4, S=64, seed=40)
+    o_all = np.lib.stride_tricks.as_strided(w.o_buf, shape=w.o_buf.shape)
+    og, lg = O.gather_request_major(o_all, w.lse_buf, w.q)
+    assert np.array_equal(og, w.notes["o_logical"]) and np.array_equal(lg, w.notes["lse_logical"])
+    g, _, _ = check(gpu_lib, w)
+    assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
+
+
+def test_page_dense_binding_helper(gpu_lib):
+    """mla_post_request_major on the whole [P, S, 12, 512] tensor equals the
+    explicit strided call."""
+    m = gpu_lib
+    w = synth.request_major("rm_helper", per=2, q=8, S=48, seed=43)
+    d = device_inputs(w)
+    base = run_debug(m, d)
+    o_all = d["o_buf"]
+    lse_all = torch.from_numpy(w.lse_buf).cuda()
+    say("request-major helper")
+    core = m.mla_post_request_major(o_all, lse_all, w.q, d["w_v"], d["w_v_scale"], d["gate"])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(core), base["core"])
+
+
+def test_compact_layout_ragged(gpu_lib):
+    """Compact request-major [R, per, q, 12, 512]: no unused rows, S = 36 (a
+    ragged last tile)."""
+    check(gpu_lib, synth.request_major("rm_compact", per=3, q=4, S=36, seed=41, compact=True))
+
+
+def test_masks(gpu_lib):
+    """kv_lens zeros (30% of partial-request pairs) and a batch ending at 33
+    of 40 tokens: masked partials count as -inf; tokens past the batch are +0."""
+    g, ref, _ = check(gpu_lib, synth.request_major("rm_masked", per=5, q=2, S=40, seed=42, kv_zero=0.3, batch_rows=33))
+    assert np.all(g["core"][33:] == 0) and np.all(g["lat"][33:] == 0)
+
+
+def test_shared_kv_row_dense_splits(gpu_lib):
+    """Dense split partials with one shared row of KV lengths ([S // q]) and
+    q = 4: a request with no KV yields +0 for its tokens."""
+    m = gpu_lib
+    w = synth.dense_splits("shared_kv", 3, 32, seed=44, p_neg_inf=0.1)
+    kv = np.array([5, 0, 7, 0, 1, 2, 0, 9], dtype=np.int32)  # R = 8 requests of 4 tokens
+    d = device_inputs(w)
+    say("shared kv row")
+    core, lat, codes, scales = m.mla_post(
+        d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], debug=True, q=4, kv_lens=torch.from_numpy(kv).cuda()
+    )
+    torch.cuda.synchronize()
+    lse = O.push_mask(w.lse_view(), 4, np.tile(kv, (3, 1)), None)
+    ref = O.mla_post(w.o_view(), lse, d["w_codes"], d["w_scales"], w.gate)
+    lat, core = to_bits(lat), to_bits(core)
+    C.check_t1(lat, ref)
+    C.check_t2(lat, codes.cpu().numpy(), scales.cpu().numpy())
+    C.check_t4(core, ref, lat, codes.cpu().numpy(), scales.cpu().numpy())
+    dead = np.repeat(kv == 0, 4)
+    assert np.all(core[dead] == 0)
+
+
+def test_no_lse_with_masks(gpu_lib):
+    """One partial without LSE: a masked request or a token past the batch
+    gives +0; every other token keeps its row bit for bit."""
+    m = gpu_lib
+    w = synth.single_partial("nolse_masked", 24, seed=45)
+    kv = np.array([3, 0, 1, 4, 0, 2], dtype=np.int32)
+    qsl = np.array([0, 4, 8, 12, 16, 20, 22], dtype=np.int32)
+    d = device_inputs(w)
+    say("no-LSE with masks")
+    core, lat, codes, scales = m.mla_post(
+        d["o"], None, d["w_v"], d["w_v_scale"], d["gate"], debug=True, q=4,
+        kv_lens=torch.from_numpy(kv).cuda(), qsl=torch.from_numpy(qsl).cuda(),
+    )
+    torch.cuda.synchronize()
+    lse = O.push_mask(np.zeros((1, 24, 12), np.float32), 4, kv[None, :], qsl)
+    ref = O.mla_post(w.o_view(), lse, d["w_codes"], d["w_scales"], w.gate)
+    lat = to_bits(lat)
+    C.check_t1(lat, ref, exact=True)
+    C.check_t4(to_bits(core), ref, strict=True)
+
+
+def test_version1_struct(gpu_lib):
+    """A caller built against the version-1 struct (struct_size 176) gets the
+    version-1 behaviour: the later fields are not read."""
+    m = gpu_lib
+    w = synth.split_merge()
+    d = device_inputs(w)
+    base = run_debug(m, d)
+    core = torch.empty((w.S, 1536), dtype=torch.bfloat16, device="cuda")
+    a = m.make_args(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], core)
+    a.struct_size = m.ARGS_V1_SIZE
+    # junk past the version-1 prefix, chosen so that validation would reject
+    # it (q not dividing S, an odd stride, a misaligned pointer) if it were read
+    a.q, a.o_sr, a.kv_lens = 7, 3, 0x11
+    say("version-1 struct")
+    st = m.load().mla_post(ctypes.byref(a), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(to_bits(core), base["core"])
