@@ -80,6 +80,13 @@ def device_setup(w, m, torch):
     return dict(o=o, lse=lse, w_v=w_v, w_s=w_s, gate=gate, core=core, o_buf=o_buf)
 
 
+def layout_args(w) -> dict:
+    """Request-major arguments of a workload (none for the dense layouts)."""
+    if w.q == 1 and not w.o_sr and not w.l_sr:
+        return {}
+    return {"q": w.q, "o_sr": w.o_sr, "l_sr": w.l_sr}
+
+
 def time_gpu(call, steps: int, warmup: int, torch) -> dict:
     for _ in range(warmup):
         call()
@@ -106,7 +113,10 @@ def cpu_baseline(w, tokens: int) -> dict:
     import oracle.post as O
 
     codes, scales = O.quantize_mxfp4(w.wv_bits)
-    o, lse = w.o_view(), w.lse_view()
+    if "o_logical" in w.notes:
+        o, lse = w.notes["o_logical"], w.notes["lse_logical"]
+    else:
+        o, lse = w.o_view(), w.lse_view()
     chunk = 64
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -205,6 +215,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument(
+        "--workload",
+        default="large_decode",
+        choices=["large_decode", "large_decode_request_major"],
+        help="large_decode: dense [16, 4096, 12, 512] partials; large_decode_request_major: the same "
+        "sizes in the request-major layout [1024 requests, 16 splits, 4 tokens, 12, 512]",
+    )
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the four other standard workloads (stderr)")
@@ -242,11 +259,11 @@ def main() -> int:
         calibrate_copy(torch)
         return 0
 
-    log("generating the large decode workload (seeded, 805 MB of partials)")
-    w = synth.large_decode()
+    log(f"generating the {args.workload} workload (seeded, 805 MB of partials)")
+    w = synth.large_decode() if args.workload == "large_decode" else synth.EXTRA[args.workload]()
     alg = algorithmic_bytes(w)
     d = device_setup(w, m, torch)
-    call = m.prepare(d["o"], d["lse"], d["w_v"], d["w_s"], d["gate"], d["core"])
+    call = m.prepare(d["o"], d["lse"], d["w_v"], d["w_s"], d["gate"], d["core"], **layout_args(w))
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     t = time_gpu(call, args.steps, args.warmup, torch)
     ms_per_step = 1e3 * t["wall_s"] / args.steps
@@ -287,7 +304,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "large_decode",
+            "workload": args.workload,
             "tokens": w.S,
             "splits": w.n,
             "heads": 12,
@@ -297,6 +314,8 @@ def main() -> int:
             "rows": alg["rows"],
             "alg_bytes_per_call": alg["alg_bytes"],
             "nominal_bytes_per_call": alg["nominal_bytes"],
+            "layout": "dense [16, 4096, 12, 512]" if args.workload == "large_decode"
+            else "request-major [1024, 16, 4, 12, 512]",
             "parallelism": "single GPU",
             "compute": "fp32 merge of bf16 rows, MXFP4 x MXFP4 MFMA, bf16 out",
         },

@@ -253,11 +253,11 @@ class Prepared:
     it enqueues the kernel on torch's current stream (for timing loops and
     serving loops that reuse the same buffers)."""
 
-    def __init__(self, o, lse, w_v, w_v_scale, gate, core, dbg=None):
+    def __init__(self, o, lse, w_v, w_v_scale, gate, core, dbg=None, **layout):
         self._lib = load()
         _need(core.is_cuda, ValueError, "tensors must be on a GPU")
-        self._keep = (o, lse, w_v, w_v_scale, gate, core, dbg)
-        self.args = make_args(o, lse, w_v, w_v_scale, gate, core, dbg)
+        self._keep = (o, lse, w_v, w_v_scale, gate, core, dbg, layout)
+        self.args = make_args(o, lse, w_v, w_v_scale, gate, core, dbg, **layout)
         self._ref = ctypes.byref(self.args)
         self.device = core.device
         _raise(self._lib, self._lib.mla_post_check(self._ref))
@@ -269,8 +269,8 @@ class Prepared:
             _raise(self._lib, st)
 
 
-def prepare(o, lse, w_v, w_v_scale, gate, core):
-    return Prepared(o, lse, w_v, w_v_scale, gate, core)
+def prepare(o, lse, w_v, w_v_scale, gate, core, **layout):
+    return Prepared(o, lse, w_v, w_v_scale, gate, core, **layout)
 
 
 def mla_post_splits(o, lse, w_v, w_v_scale, gate, core=None, debug=False):

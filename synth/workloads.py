@@ -209,6 +209,8 @@ def request_major(
     p_neg_inf: float = 0.1,
     kv_zero: float = 0.0,
     batch_rows: int | None = None,
+    o_sigma: float = 1.0,
+    lse_normal: tuple | None = None,
 ) -> Workload:
     """Split partials laid out request-major, R = S / q requests of q tokens,
     per splits each.
@@ -226,8 +228,11 @@ def request_major(
     assert S % q == 0
     R = S // q
     rng = np.random.Generator(np.random.PCG64(seed))
-    vals = _normal_bf16(rng, (per, S, NH, KVL), 1.0)
-    lv = rng.uniform(-4.0, 16.0, size=(per, S, NH)).astype(np.float32)
+    vals = _normal_bf16(rng, (per, S, NH, KVL), o_sigma)
+    if lse_normal is not None:
+        lv = rng.normal(lse_normal[0], lse_normal[1], size=(per, S, NH)).astype(np.float32)
+    else:
+        lv = rng.uniform(-4.0, 16.0, size=(per, S, NH)).astype(np.float32)
     u = rng.random((per, S, NH))
     lv[u < p_neg_inf] = -np.inf
     kv = rng.integers(1, 65, size=(per, R)).astype(np.int32)
@@ -296,6 +301,16 @@ def large_decode() -> Workload:
     return dense_splits("large_decode", 16, 4096, seed=4, o_sigma=2.0, lse_normal=(8.0, 6.0), p_neg_inf=0.05)
 
 
+def large_decode_request_major() -> Workload:
+    """The large decode batch's sizes and distributions (S=4096, 1024
+    requests x 4 tokens, 16 splits, o ~N(0,2), lse ~N(8,6) with 5% -inf) in
+    the compact request-major layout [1024, 16, 4, 12, 512]; seed 5."""
+    return request_major(
+        "large_decode_request_major", per=16, q=4, S=4096, seed=5, compact=True, p_neg_inf=0.05,
+        o_sigma=2.0, lse_normal=(8.0, 6.0),
+    )
+
+
 STANDARD = {
     "tiny": tiny,
     "no_merge": no_merge,
@@ -303,6 +318,8 @@ STANDARD = {
     "dcp8": dcp8,
     "large_decode": large_decode,
 }
+
+EXTRA = {"large_decode_request_major": large_decode_request_major}
 
 
 def live_rows(w: Workload) -> int:
@@ -314,5 +331,5 @@ def live_rows(w: Workload) -> int:
     """
     if w.lse_buf is None:
         return w.n * w.S * NH
-    v = w.lse_view()
+    v = w.notes["lse_logical"] if "lse_logical" in w.notes else w.lse_view()
     return int(np.isfinite(v).sum())
