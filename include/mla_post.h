@@ -88,8 +88,8 @@ typedef struct mla_post_args {
                                 (h, v, b) at + h*s_sh + v*s_sv + b*s_sb */
   int64_t s_sh, s_sv, s_sb;  /* bytes, >= 0 */
 
-  const void* gate; /* bf16 [S, 1536] dense, 8-byte aligned */
-  void* core;       /* bf16 [S, 1536] dense, 8-byte aligned; every row t < S is
+  const void* gate; /* bf16 [S, 1536] dense, 16-byte aligned */
+  void* core;       /* bf16 [S, 1536] dense, 16-byte aligned; every row t < S is
                        written, nothing else is */
 
   /* Optional stage outputs (NULL to skip), written by the same kernel with

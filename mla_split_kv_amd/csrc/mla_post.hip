@@ -7,19 +7,23 @@
 // -> MXFP4 -> scaled FP4 MFMA against W_V[h] -> bf16 x gate -> core.
 //
 // Decomposition (this library's own, not the page's):
-//   workgroup = (head h, 16 tokens), 8 waves of 64 lanes;
-//   merge: wave w owns tokens 2w and 2w+1 of the tile; a token's partial row
-//     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced 16-byte load
-//     per lane, and a wave keeps ROWS_IN_FLIGHT rows in flight;
+//   workgroup = 8 waves of 64 lanes that own one head h for the whole launch
+//     and walk its 16-token tiles (k workgroups per head, k filling the
+//     device once); W_V[h]'s operands stay in registers throughout;
+//   merge: per tile, wave w owns tokens 2w and 2w+1; a token's partial row
+//     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced non-temporal
+//     16-byte load per lane, ROWS_IN_FLIGHT rows in flight, rows of weight 0
+//     not loaded; the next tile's LSEs are loaded a tile ahead;
 //   the merged latents never go to memory: each lane rounds its 8 latents
 //     to bf16, the 4 lanes of a 32-element block agree on the E8M0 code with
 //     two DPP steps, and the hardware scaled convert packs the 8 FP4 codes;
-//     codes and scales are staged in LDS as the MFMA B operand;
-//   W_UV: wave w multiplies W_V[h] rows 16w..16w+15 (A operand, prefetched
-//     into registers before the merge) by the 16 tokens' latent codes, four
-//     16x16x128 scaled FP4 MFMAs over K = 512, so all 16 MFMA columns carry
-//     live tokens (the page fills 4 of 16);
-//   epilogue: bf16(acc) x gate -> bf16, 8-byte stores, tokens < S only.
+//     codes and scales go to (double-buffered) LDS as the MFMA B operand;
+//   W_UV: wave w multiplies W_V[h] rows 16w..16w+15 (A operand) by the 16
+//     tokens' latent codes, four 16x16x128 scaled FP4 MFMAs over K = 512, so
+//     all 16 MFMA columns carry live tokens (the page fills 4 of 16);
+//   epilogue: bf16(acc) tiles are held in LDS and written when the
+//     workgroup's tiles are done: x gate -> bf16, 16-byte non-temporal
+//     stores, tokens < S only.
 
 #include <hip/hip_runtime.h>
 
@@ -43,19 +47,18 @@ constexpr int THREADS = WAVES * 64;            // 512
 constexpr int TOK_PER_WAVE = TILE_T / WAVES;   // 2
 constexpr int ROWS_IN_FLIGHT = 8;              // partial rows a wave loads before it sums
 constexpr bool NT_ROWS = true;                 // partial rows loaded non-temporally
-constexpr bool LATE_WV = false;                // W_V operands loaded after the merge, not before
-// A token tile's 12 heads on one XCD (xcd_task): measured on the large decode
-// workload it removes the duplicate L2 fetches (HBM reads 804 -> 784 MB per
-// launch) but runs 2.5% slower (134.1 -> 137.4 us), so it is off.
-constexpr bool XCD_REMAP = false;
-constexpr int NXCD = 8;                        // XCDs of an MI355X
+constexpr int WG_PER_CU = 3;                   // resident workgroups per CU at this register budget
 #ifndef MLA_KERNEL_ATTRS
 #define MLA_KERNEL_ATTRS
 #endif
 constexpr int NBLK = KVL / 32;                 // 16 MXFP4 blocks per latent row
 constexpr int CODE_ROW = TILE_T * 16 + 16;     // LDS bytes per block row (+16 B skew)
-constexpr int LDS_CODES = NBLK * CODE_ROW;     // 4352 B
-constexpr int LDS_SCALES = TILE_T * NBLK;      // 256 B
+constexpr int LDS_CODES = NBLK * CODE_ROW;     // 4352 B per buffer
+constexpr int LDS_SCALES = TILE_T * NBLK;      // 256 B per buffer
+constexpr int OUT_ROW = VD * 2 + 16;           // LDS bytes per token of the output tile (+16 B skew)
+constexpr int LDS_OUT = TILE_T * OUT_ROW;      // 4352 B
+constexpr int STORE_LANES = TILE_T * VD * 2 / 16;  // 256 16-byte pieces per output tile
+constexpr int OUT_TILES = 8;                   // output tiles held in LDS before they are written
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -93,10 +96,6 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float round_bf16(float x) {
-  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) << 16);
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -188,13 +187,28 @@ __device__ __forceinline__ void lse_to_weights(float l[NCH]) {
   for (int c = 0; c < NCH; ++c) l[c] = (tot == 0.f || l[c] == 0.f) ? 0.f : l[c] / tot;
 }
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// 16 bytes with the non-temporal (streaming) hint, for data touched once.
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// core is written once and not read back by this kernel: a streaming store.
+// Measured on the large decode batch, the 12.6 MB of core writes cost about
+// 18 us of a 131 us access skeleton as ordinary stores and 13 us as
+// non-temporal ones (they compete with the read stream).
+__device__ __forceinline__ void store_nt16(uint8_t* p, const uint4& v) {
+  const v4u t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<v4u*>(p));
+}
+
 // One 1 KiB partial row: 16 B per lane. The rows are read once, so they are
 // loaded non-temporally and do not push W_V out of L2.
 __device__ __forceinline__ uint4 load_row16(const uint8_t* p, int lane) {
   if constexpr (NT_ROWS) {
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + lane);
-    return make_uint4(t.x, t.y, t.z, t.w);
+    return load_nt16(p + 16 * lane);
   } else {
     return reinterpret_cast<const uint4*>(p)[lane];
   }
@@ -290,86 +304,130 @@ __device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h
   }
 }
 
-// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8),
-// and each XCD has its own L2. Task = (token tile, head), head-minor; the
-// remap gives each XCD a contiguous run of tasks, so the 12 heads of a token
-// tile run on one XCD at about the same time and share its L2 lines of LSEs
-// (12 heads interleaved every 48 B) and neighbouring partial rows. The
-// remainder of the grid past the last multiple of 8 maps to itself.
-__device__ __forceinline__ int xcd_task(int b, int nblocks) {
-  if constexpr (!XCD_REMAP) return b;
-  const int full = nblocks & ~(NXCD - 1);
-  if (b >= full) return b;
-  return (b % NXCD) * (full / NXCD) + b / NXCD;
+// Sanitised LSEs of this wave's two tokens of token tile `tile` (all -inf for
+// tokens past S or past the batch, or when the tile does not exist).
+template <int NCH>
+__device__ __forceinline__ void prefetch_lse(const KArgs& a, int tile, int batch_end, int h, int wave, int lane,
+                                             float lA[NCH], float lB[NCH]) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) lA[c] = lB[c] = -INFINITY;
+  const int tA = tile * TILE_T + wave * TOK_PER_WAVE, tB = tA + 1;
+  if (tA < a.S && tA < batch_end) load_lse<NCH>(a, tA, tA / a.q, h, lane, lA);
+  if (tB < a.S && tB < batch_end) load_lse<NCH>(a, tB, tB / a.q, h, lane, lB);
+}
+
+// Write `count` staged output tiles of head h (tiles first, first + step, ..):
+// core = bf16( bf16(acc) * gate ); the product of two bf16 values is exact in
+// float32, so that is one rounding. Each token's 256 bytes of the head go out
+// as 16 coalesced 16-byte pieces; the whole workgroup shares the pieces.
+__device__ __forceinline__ void flush_tiles(const KArgs& a, int h, int first, int step, int count,
+                                            uint8_t (*s_out)[LDS_OUT]) {
+  for (int i = threadIdx.x; i < count * STORE_LANES; i += THREADS) {
+    const int k = i / STORE_LANES, piece = i % STORE_LANES;
+    const int tok = piece >> 4, col = (piece & 15) * 8;
+    const int t = (first + k * step) * TILE_T + tok;
+    if (t >= a.S) continue;
+    const int64_t off = ((int64_t)t * GROWS + h * VD + col) * 2;
+    const uint4 g8 = load_nt16(a.gate + off);
+    const uint4 av = *reinterpret_cast<const uint4*>(s_out[k] + tok * OUT_ROW + col * 2);
+    const uint4 out = make_uint4(pack_bf16(bf_lo(av.x) * bf_lo(g8.x), bf_hi(av.x) * bf_hi(g8.x)),
+                                 pack_bf16(bf_lo(av.y) * bf_lo(g8.y), bf_hi(av.y) * bf_hi(g8.y)),
+                                 pack_bf16(bf_lo(av.z) * bf_lo(g8.z), bf_hi(av.z) * bf_hi(g8.z)),
+                                 pack_bf16(bf_lo(av.w) * bf_lo(g8.w), bf_hi(av.w) * bf_hi(g8.w)));
+    store_nt16(a.core + off, out);
+  }
 }
 
 // ---------------------------------------------------------------- the fused kernel
 
 template <bool NOLSE, int NCH>
-__global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
+__global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
+  // two LDS buffers: a wave may merge tile i+1 while others still read tile i
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[OUT_TILES][LDS_OUT];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int task = xcd_task(blockIdx.x, gridDim.x);
-  const int h = task % NH;
-  const int t0 = (task / NH) * TILE_T;
+  const int h = blockIdx.x % NH;      // this workgroup's head, fixed
+  const int slot = blockIdx.x / NH;   // its token tiles: slot, slot + wg_per_head, ...
+  const int ntiles = (a.S + TILE_T - 1) / TILE_T;
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
+  // W_V[h]'s operands for this wave's 16 rows stay in registers for every
+  // tile of the head.
   uint4 wv[4];
   int sa = 0;
-  if constexpr (!LATE_WV) load_wv(a, h, wave, tl, kb, wv, sa);
-
-  // ---- merge + quantise: wave owns tile slots 2 wave and 2 wave + 1
-  const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
-  const int tA = t0 + ttA, tB = t0 + ttB;
-  const bool liveA = tA < a.S, liveB = tB < a.S;
+  load_wv(a, h, wave, tl, kb, wv, sa);
   // tokens at or past qsl[R] lie past the batch: every partial is empty
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
-  const bool emptyA = tA >= batch_end, emptyB = tB >= batch_end;
-  float wA[NCH], wB[NCH];
-  if constexpr (!NOLSE) {
-    // both tokens' LSE loads in flight before either reduction
+
+  // LSEs of this wave's two tokens, loaded one tile ahead: the next tile's
+  // loads are issued before this tile's barrier, MFMAs and stores, so their
+  // latency is hidden behind them.
+  float lA[NCH], lB[NCH];
+  if constexpr (!NOLSE) prefetch_lse<NCH>(a, slot, batch_end, h, wave, lane, lA, lB);
+
+#pragma unroll 1
+  for (int tile = slot, it = 0; tile < ntiles; tile += wg_per_head, ++it) {
+    uint8_t* codes = s_codes[it & 1];
+    uint8_t* scales = s_scales[it & 1];
+    const int t0 = tile * TILE_T;
+
+    // ---- merge + quantise: wave owns tile slots 2 wave and 2 wave + 1
+    const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
+    const int tA = t0 + ttA, tB = t0 + ttB;
+    const bool liveA = tA < a.S, liveB = tB < a.S;
+    const bool emptyA = tA >= batch_end, emptyB = tB >= batch_end;
+    float wA[NCH], wB[NCH];
+    if constexpr (!NOLSE) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) wA[c] = wB[c] = -INFINITY;
-    if (liveA && !emptyA) load_lse<NCH>(a, tA, tA / a.q, h, lane, wA);
-    if (liveB && !emptyB) load_lse<NCH>(a, tB, tB / a.q, h, lane, wB);
-    if (liveA && !emptyA) lse_to_weights<NCH>(wA);
-    if (liveB && !emptyB) lse_to_weights<NCH>(wB);
-  }
-  token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, emptyA, wA, s_codes, s_scales);
-  token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, emptyB, wB, s_codes, s_scales);
-  if constexpr (LATE_WV) load_wv(a, h, wave, tl, kb, wv, sa);
-  __syncthreads();
+      for (int c = 0; c < NCH; ++c) {
+        wA[c] = lA[c];
+        wB[c] = lB[c];
+      }
+      if (liveA && !emptyA) lse_to_weights<NCH>(wA);
+      if (liveB && !emptyB) lse_to_weights<NCH>(wB);
+    }
+    token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, emptyA, wA, codes, scales);
+    token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, emptyB, wB, codes, scales);
+    if constexpr (!NOLSE) prefetch_lse<NCH>(a, tile + wg_per_head, batch_end, h, wave, lane, lA, lB);
+    // One barrier per tile: it publishes this tile's codes, and since every
+    // wave finished the previous tile's MFMAs before merging this one, the
+    // other buffer is free for the next tile.
+    __syncthreads();
 
-  // ---- W_UV: D[v][token] = sum_k W_V[h][v][k] * L[token][k]
-  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  {
-    const uint8_t* brow = s_codes + tl * 16;
-    acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
-    acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
-    acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
-    acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
-  }
-  // The MFMAs read operands from all 64 lanes: they must run with the whole
-  // wave active. Pinning the result here keeps the compiler from sinking them
-  // into the per-lane store condition below (where a ragged tile masks lanes).
-  asm volatile("" : "+v"(acc));
+    // ---- W_UV: D[v][token] = sum_k W_V[h][v][k] * L[token][k]
+    const int sb = *reinterpret_cast<const int*>(scales + tl * NBLK + kb * 4);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* brow = codes + tl * 16;
+      acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
+      acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
+      acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
+      acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    }
+    // The MFMAs read operands from all 64 lanes: they must run with the whole
+    // wave active. Pinning the result here keeps the compiler from sinking
+    // them into the per-lane store condition below (where a ragged tile masks
+    // lanes).
+    asm volatile("" : "+v"(acc));
 
-  // ---- gate and store ([mla_back: stage_uv]): lane holds rows v0..v0+3 of token tl
-  const int t = t0 + tl;
-  if (t < a.S) {
-    const int col = h * VD + wave * 16 + kb * 4;
-    const int64_t off = ((int64_t)t * GROWS + col) * 2;
-    const uint2 g = *reinterpret_cast<const uint2*>(a.gate + off);
-    const float o0 = round_bf16(acc[0]) * bf_lo(g.x);
-    const float o1 = round_bf16(acc[1]) * bf_hi(g.x);
-    const float o2 = round_bf16(acc[2]) * bf_lo(g.y);
-    const float o3 = round_bf16(acc[3]) * bf_hi(g.y);
-    *reinterpret_cast<uint2*>(a.core + off) = make_uint2(pack_bf16(o0, o1), pack_bf16(o2, o3));
+    // ---- stage bf16(acc) ([mla_back: stage_uv]): the lane holds rows
+    // v0..v0+3 (v0 = 16 wave + 4 kb) of token tl. Tiles are kept in LDS and
+    // written (times the gate) when OUT_TILES have gathered or the
+    // workgroup's tiles are done: the writes then come in bursts, mostly
+    // after the read stream, instead of competing with it all along.
+    const int slot_out = it % OUT_TILES;
+    *reinterpret_cast<uint2*>(s_out[slot_out] + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
+        make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+    const bool last = tile + wg_per_head >= ntiles;
+    if (slot_out == OUT_TILES - 1 || last) {
+      __syncthreads();
+      flush_tiles(a, h, tile - slot_out * wg_per_head, wg_per_head, slot_out + 1, s_out);
+      if (!last) __syncthreads();  // the staging buffers are reused
+    }
   }
 }
 
@@ -452,7 +510,7 @@ int check_args(const mla_post_args* in) {
   if (a->lse && (a->l_sj < 0 || a->l_st < 0 || a->l_sh < 0)) return MLA_POST_ESTRIDE;
   if (a->w_sh < 0 || a->w_sv < 0 || (a->w_sh % 16) || (a->w_sv % 16)) return MLA_POST_ESTRIDE;
   if (a->s_sh < 0 || a->s_sv < 0 || a->s_sb < 0) return MLA_POST_ESTRIDE;
-  if (!aligned(a->o, 16) || !aligned(a->w_v, 16) || !aligned(a->gate, 8) || !aligned(a->core, 8))
+  if (!aligned(a->o, 16) || !aligned(a->w_v, 16) || !aligned(a->gate, 16) || !aligned(a->core, 16))
     return MLA_POST_EALIGN;
   if (a->lse && !aligned(a->lse, 4)) return MLA_POST_EALIGN;
   if ((a->dbg_lat && !aligned(a->dbg_lat, 16)) || (a->dbg_codes && !aligned(a->dbg_codes, 4))) return MLA_POST_EALIGN;
@@ -481,10 +539,22 @@ int check_args(const mla_post_args* in) {
   return MLA_POST_OK;
 }
 
+// Workgroups per head: enough to fill the device once (WG_PER_CU resident
+// workgroups on each CU), or one per token tile when there are fewer tiles.
+int workgroups_per_head(int S) {
+  const int ntiles = (S + TILE_T - 1) / TILE_T;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int fill = (cus * WG_PER_CU) / NH;
+  return ntiles < fill ? ntiles : (fill > 0 ? fill : 1);
+}
+
 template <bool NOLSE, int NCH>
 int launch(const KArgs& k, int S, hipStream_t stream) {
-  const unsigned grid = (unsigned)(NH * ((S + TILE_T - 1) / TILE_T));
-  hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k);
+  const int wph = workgroups_per_head(S);
+  const unsigned grid = (unsigned)(NH * wph);
+  hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k, wph);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_hip_error = hipGetErrorString(e);

@@ -111,6 +111,8 @@ def test_valid_args_pass(lib):
         ("w_v", 0x300004, EALIGN),
         ("gate", 0x500002, EALIGN),
         ("core", 0x600004, EALIGN),
+        ("core", 0x600008, EALIGN),  # 16-byte output stores
+        ("gate", 0x500008, EALIGN),
         ("lse", 0x200002, EALIGN),
         ("o_sj", 1 << 61, ERANGE),
         ("l_sj", 1 << 62, ERANGE),
