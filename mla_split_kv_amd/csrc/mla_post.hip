@@ -214,6 +214,18 @@ __device__ __forceinline__ uint4 load_row16(const uint8_t* p, int lane) {
   }
 }
 
+// acc[0..7] += w * (the 8 bf16 values of a lane's 16 bytes of a row)
+__device__ __forceinline__ void fma_row(float w, const uint4& v, float acc[8]) {
+  acc[0] = fmaf(w, bf_lo(v.x), acc[0]);
+  acc[1] = fmaf(w, bf_hi(v.x), acc[1]);
+  acc[2] = fmaf(w, bf_lo(v.y), acc[2]);
+  acc[3] = fmaf(w, bf_hi(v.y), acc[3]);
+  acc[4] = fmaf(w, bf_lo(v.z), acc[4]);
+  acc[5] = fmaf(w, bf_hi(v.z), acc[5]);
+  acc[6] = fmaf(w, bf_lo(v.w), acc[6]);
+  acc[7] = fmaf(w, bf_hi(v.w), acc[7]);
+}
+
 // Weighted sum of the partial rows of (t, h) for this lane's 8 latents
 // [k = 8 lane .. 8 lane + 7], skipping rows of weight 0 (not even loaded).
 template <int NCH>
@@ -236,17 +248,7 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, const uint8_t* rowbas
         if (wb & 0x7FFFFFFF) v[b] = load_row16(rowbase + (int64_t)(64 * c + jl) * a.o_sj, lane);
       }
 #pragma unroll
-      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) {
-        const float w = wj[b];
-        acc[0] = fmaf(w, bf_lo(v[b].x), acc[0]);
-        acc[1] = fmaf(w, bf_hi(v[b].x), acc[1]);
-        acc[2] = fmaf(w, bf_lo(v[b].y), acc[2]);
-        acc[3] = fmaf(w, bf_hi(v[b].y), acc[3]);
-        acc[4] = fmaf(w, bf_lo(v[b].z), acc[4]);
-        acc[5] = fmaf(w, bf_hi(v[b].z), acc[5]);
-        acc[6] = fmaf(w, bf_lo(v[b].w), acc[6]);
-        acc[7] = fmaf(w, bf_hi(v[b].w), acc[7]);
-      }
+      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) fma_row(wj[b], v[b], acc);
     }
   }
 }
@@ -265,31 +267,11 @@ __device__ __forceinline__ void load_wv(const KArgs& a, int h, int wave, int tl,
   for (int st = 0; st < 4; ++st) sa |= (int)srow[(st * 4 + kb) * a.s_sb] << (8 * st);
 }
 
-// Latents of token t (tile slot tt) -> bf16 -> MXFP4 codes and scale into
-// LDS (the MFMA B operand) and, if asked, the stage outputs.
-// `empty`: every partial of token t is masked (past the batch), so the
-// latents are +0 without reading anything.
-template <bool NOLSE, int NCH>
-__device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
-                                            const float wts[NCH], uint8_t* s_codes, uint8_t* s_scales) {
-  uint32_t lat[4] = {0u, 0u, 0u, 0u};
-  if (live && !empty) {
-    const int r = t / a.q;
-    const uint8_t* rowbase = a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (int64_t)r * a.o_sr;
-    if constexpr (NOLSE) {
-      // one partial and no LSE: the row is the attention output itself
-      // (unless its request is masked as having no KV)
-      if (!(a.kv_lens && a.kv_lens[r] == 0)) {
-        const uint4 v = load_row16(rowbase, lane);
-        lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
-      }
-    } else {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      merge_rows<NCH>(a, rowbase, lane, wts, acc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
-    }
-  }
+// bf16 latents of token t (tile slot tt) -> MXFP4 codes and scale into LDS
+// (the MFMA B operand) and, if asked, the stage outputs. Slots of tokens past
+// S get zero codes.
+__device__ __forceinline__ void quant_to_lds(const KArgs& a, int t, int tt, int h, int lane, bool live,
+                                             const uint32_t lat[4], uint8_t* s_codes, uint8_t* s_scales) {
   int code;
   const uint32_t pk = quant8(lat, code);
   const int b = lane >> 2;  // this lane's block
@@ -304,6 +286,36 @@ __device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h
   }
 }
 
+__device__ __forceinline__ const uint8_t* row_base(const KArgs& a, int t, int h) {
+  return a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (int64_t)(t / a.q) * a.o_sr;
+}
+
+// Latents of token t (tile slot tt) -> bf16 -> MXFP4 into LDS.
+// `empty`: every partial of token t is masked (past the batch), so the
+// latents are +0 without reading anything.
+template <bool NOLSE, int NCH>
+__device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
+                                            const float wts[NCH], uint8_t* s_codes, uint8_t* s_scales) {
+  uint32_t lat[4] = {0u, 0u, 0u, 0u};
+  if (live && !empty) {
+    const uint8_t* rowbase = row_base(a, t, h);
+    if constexpr (NOLSE) {
+      // one partial and no LSE: the row is the attention output itself
+      // (unless its request is masked as having no KV)
+      if (!(a.kv_lens && a.kv_lens[t / a.q] == 0)) {
+        const uint4 v = load_row16(rowbase, lane);
+        lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+      }
+    } else {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      merge_rows<NCH>(a, rowbase, lane, wts, acc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
+    }
+  }
+  quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
+}
+
 // Sanitised LSEs of this wave's two tokens of token tile `tile` (all -inf for
 // tokens past S or past the batch, or when the tile does not exist).
 template <int NCH>
@@ -314,6 +326,15 @@ __device__ __forceinline__ void prefetch_lse(const KArgs& a, int tile, int batch
   const int tA = tile * TILE_T + wave * TOK_PER_WAVE, tB = tA + 1;
   if (tA < a.S && tA < batch_end) load_lse<NCH>(a, tA, tA / a.q, h, lane, lA);
   if (tB < a.S && tB < batch_end) load_lse<NCH>(a, tB, tB / a.q, h, lane, lB);
+}
+
+// 8 bf16 W_UV results times 8 bf16 gate values, each rounded once to bf16
+// (the product of two bf16 values is exact in float32).
+__device__ __forceinline__ uint4 gate_mul(const uint4& av, const uint4& g8) {
+  return make_uint4(pack_bf16(bf_lo(av.x) * bf_lo(g8.x), bf_hi(av.x) * bf_hi(g8.x)),
+                    pack_bf16(bf_lo(av.y) * bf_lo(g8.y), bf_hi(av.y) * bf_hi(g8.y)),
+                    pack_bf16(bf_lo(av.z) * bf_lo(g8.z), bf_hi(av.z) * bf_hi(g8.z)),
+                    pack_bf16(bf_lo(av.w) * bf_lo(g8.w), bf_hi(av.w) * bf_hi(g8.w)));
 }
 
 // Write `count` staged output tiles of head h (tiles first, first + step, ..):
@@ -330,11 +351,7 @@ __device__ __forceinline__ void flush_tiles(const KArgs& a, int h, int first, in
     const int64_t off = ((int64_t)t * GROWS + h * VD + col) * 2;
     const uint4 g8 = load_nt16(a.gate + off);
     const uint4 av = *reinterpret_cast<const uint4*>(s_out[k] + tok * OUT_ROW + col * 2);
-    const uint4 out = make_uint4(pack_bf16(bf_lo(av.x) * bf_lo(g8.x), bf_hi(av.x) * bf_hi(g8.x)),
-                                 pack_bf16(bf_lo(av.y) * bf_lo(g8.y), bf_hi(av.y) * bf_hi(g8.y)),
-                                 pack_bf16(bf_lo(av.z) * bf_lo(g8.z), bf_hi(av.z) * bf_hi(g8.z)),
-                                 pack_bf16(bf_lo(av.w) * bf_lo(g8.w), bf_hi(av.w) * bf_hi(g8.w)));
-    store_nt16(a.core + off, out);
+    store_nt16(a.core + off, gate_mul(av, g8));
   }
 }
 
@@ -428,6 +445,114 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
       flush_tiles(a, h, tile - slot_out * wg_per_head, wg_per_head, slot_out + 1, s_out);
       if (!last) __syncthreads();  // the staging buffers are reused
     }
+  }
+}
+
+// ---------------------------------------------------------------- the latency-regime kernel
+
+// When the whole grid is resident at once (one token tile per workgroup) and
+// n <= LAT_NMAX, bandwidth is not the bound; the chain of dependent memory
+// round trips is (LSEs -> weights -> rows of one token -> rows of the other
+// -> gate). This kernel issues everything at once: W_V, the gate, the LSEs
+// and every partial row of both tokens, speculatively, before the weights
+// are known; a row whose weight turns out to be 0 is then left out of the
+// sum by a uniform branch, so NaN or inf stored in it cannot reach the
+// result. Same arithmetic, same order of summation as the main kernel.
+constexpr int LAT_NMAX = 8;
+
+template <bool NOLSE>
+__global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[LDS_OUT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.x % NH;
+  const int tile = blockIdx.x / NH;
+  const int t0 = tile * TILE_T;
+  const int tl = lane & 15;
+  const int kb = lane >> 4;
+  const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
+
+  uint4 wv[4];
+  int sa = 0;
+  load_wv(a, h, wave, tl, kb, wv, sa);
+  // the gate piece this thread writes at the end (token i / 16, 8 columns)
+  const int tok = threadIdx.x >> 4, col = (threadIdx.x & 15) * 8;
+  const int t_out = t0 + tok;
+  const bool out_live = threadIdx.x < STORE_LANES && t_out < a.S;
+  const int64_t out_off = ((int64_t)t_out * GROWS + h * VD + col) * 2;
+  uint4 g8 = make_uint4(0u, 0u, 0u, 0u);
+  if (out_live) g8 = load_nt16(a.gate + out_off);
+
+  const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
+  const int tA = t0 + ttA, tB = t0 + ttB;
+  const bool liveA = tA < a.S, liveB = tB < a.S;
+  const bool useA = liveA && tA < batch_end, useB = liveB && tB < batch_end;
+  uint32_t latA[4] = {0u, 0u, 0u, 0u}, latB[4] = {0u, 0u, 0u, 0u};
+  if constexpr (NOLSE) {
+    if (useA && !(a.kv_lens && a.kv_lens[tA / a.q] == 0)) {
+      const uint4 v = load_row16(row_base(a, tA, h), lane);
+      latA[0] = v.x; latA[1] = v.y; latA[2] = v.z; latA[3] = v.w;
+    }
+    if (useB && !(a.kv_lens && a.kv_lens[tB / a.q] == 0)) {
+      const uint4 v = load_row16(row_base(a, tB, h), lane);
+      latB[0] = v.x; latB[1] = v.y; latB[2] = v.z; latB[3] = v.w;
+    }
+  } else {
+    float lA[1] = {-INFINITY}, lB[1] = {-INFINITY};
+    if (useA) load_lse<1>(a, tA, tA / a.q, h, lane, lA);
+    if (useB) load_lse<1>(a, tB, tB / a.q, h, lane, lB);
+    uint4 rA[LAT_NMAX], rB[LAT_NMAX];
+    const uint8_t* baseA = row_base(a, tA, h);
+    const uint8_t* baseB = row_base(a, tB, h);
+#pragma unroll
+    for (int j = 0; j < LAT_NMAX; ++j) {
+      rA[j] = rB[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (useA && j < a.n) rA[j] = load_row16(baseA + (int64_t)j * a.o_sj, lane);
+      if (useB && j < a.n) rB[j] = load_row16(baseB + (int64_t)j * a.o_sj, lane);
+    }
+    if (useA) lse_to_weights<1>(lA);
+    if (useB) lse_to_weights<1>(lB);
+    float accA[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float accB[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < LAT_NMAX; ++j) {
+      const int wa = useA && j < a.n ? __builtin_amdgcn_readlane(__float_as_int(lA[0]), j) : 0;
+      const int wb = useB && j < a.n ? __builtin_amdgcn_readlane(__float_as_int(lB[0]), j) : 0;
+      if (wa & 0x7FFFFFFF) fma_row(__int_as_float(wa), rA[j], accA);
+      if (wb & 0x7FFFFFFF) fma_row(__int_as_float(wb), rB[j], accB);
+    }
+    if (useA) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) latA[k] = pack_bf16(accA[2 * k], accA[2 * k + 1]);
+    }
+    if (useB) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) latB[k] = pack_bf16(accB[2 * k], accB[2 * k + 1]);
+    }
+  }
+  quant_to_lds(a, tA, ttA, h, lane, liveA, latA, s_codes, s_scales);
+  quant_to_lds(a, tB, ttB, h, lane, liveB, latB, s_codes, s_scales);
+  __syncthreads();
+
+  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const uint8_t* brow = s_codes + tl * 16;
+    acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
+  }
+  asm volatile("" : "+v"(acc));  // MFMAs with the whole wave active (see the main kernel)
+  *reinterpret_cast<uint2*>(s_out + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
+      make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+  __syncthreads();
+  if (out_live) {
+    const uint4 av = *reinterpret_cast<const uint4*>(s_out + tok * OUT_ROW + col * 2);
+    store_nt16(a.core + out_off, gate_mul(av, g8));
   }
 }
 
@@ -550,9 +675,23 @@ int workgroups_per_head(int S) {
   return ntiles < fill ? ntiles : (fill > 0 ? fill : 1);
 }
 
+int launched(hipError_t e) {
+  if (e != hipSuccess) {
+    g_hip_error = hipGetErrorString(e);
+    return MLA_POST_ELAUNCH;
+  }
+  return MLA_POST_OK;
+}
+
 template <bool NOLSE, int NCH>
 int launch(const KArgs& k, int S, hipStream_t stream) {
+  const int ntiles = (S + TILE_T - 1) / TILE_T;
   const int wph = workgroups_per_head(S);
+  if (wph == ntiles && NCH == 1 && (NOLSE || k.n <= LAT_NMAX)) {
+    // latency regime: one tile per workgroup, everything issued up front
+    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE>), dim3((unsigned)(NH * ntiles)), dim3(THREADS), 0, stream, k);
+    return launched(hipGetLastError());
+  }
   const unsigned grid = (unsigned)(NH * wph);
   hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k, wph);
   hipError_t e = hipGetLastError();

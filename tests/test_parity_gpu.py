@@ -105,6 +105,10 @@ def test_large_decode_sampled(gpu_lib):
         pytest.param(lambda: synth.dense_splits("wide_lse", 12, 24, seed=17, lse_normal=(0.0, 80.0)), id="wide_lse_spread"),
         pytest.param(lambda: synth.dcp_gathered("dcp3_pad", 3, 29, seed=18, head_stride_rows=40, dead_from=20), id="dcp3_padded"),
         pytest.param(lambda: synth.single_partial("no_merge_S5", 5, seed=19, o_sigma=300.0), id="no_merge_ragged"),
+        # S past one device-filling wave of workgroups (more than 64 tiles per
+        # head at 256 CUs): the persistent kernel, with a ragged last tile
+        pytest.param(lambda: synth.dense_splits("persistent_ragged", 3, 1030, seed=23, p_neg_inf=0.2), id="persistent_ragged"),
+        pytest.param(lambda: synth.single_partial("persistent_no_lse", 1100, seed=24), id="persistent_no_lse"),
     ],
 )
 def test_edge(gpu_lib, w):
