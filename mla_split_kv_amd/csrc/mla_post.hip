@@ -189,6 +189,14 @@ __device__ __forceinline__ void lse_to_weights(float l[NCH]) {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// 8 bytes with the non-temporal hint (gate values, read once).
+__device__ __forceinline__ uint2 load_nt8(const uint8_t* p) {
+  const v2u t = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  return make_uint2(t.x, t.y);
+}
+
 // 16 bytes with the non-temporal (streaming) hint, for data touched once.
 __device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
   const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
@@ -206,12 +214,16 @@ __device__ __forceinline__ void store_nt16(uint8_t* p, const uint4& v) {
 
 // One 1 KiB partial row: 16 B per lane. The rows are read once, so they are
 // loaded non-temporally and do not push W_V out of L2.
+// The row start p is the same for the whole wave: it goes into a scalar
+// buffer resource that covers exactly the row's 1024 bytes, and the lane's
+// 16 bytes are fetched at offset 16 lane (one vector register for every row,
+// instead of a 64-bit address per row; an offset past the row would read 0).
+constexpr int BUF_WORD3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 __device__ __forceinline__ uint4 load_row16(const uint8_t* p, int lane) {
-  if constexpr (NT_ROWS) {
-    return load_nt16(p + 16 * lane);
-  } else {
-    return reinterpret_cast<const uint4*>(p)[lane];
-  }
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, KVL * 2, BUF_WORD3);
+  const v4u t = (v4u)__builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, NT_ROWS ? 2 : 0);  // 2: nt
+  return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 // acc[0..7] += w * (the 8 bf16 values of a lane's 16 bytes of a row)
@@ -337,10 +349,9 @@ __device__ __forceinline__ uint4 gate_mul(const uint4& av, const uint4& g8) {
                     pack_bf16(bf_lo(av.w) * bf_lo(g8.w), bf_hi(av.w) * bf_hi(g8.w)));
 }
 
-// Write `count` staged output tiles of head h (tiles first, first + step, ..):
-// core = bf16( bf16(acc) * gate ); the product of two bf16 values is exact in
-// float32, so that is one rounding. Each token's 256 bytes of the head go out
-// as 16 coalesced 16-byte pieces; the whole workgroup shares the pieces.
+// Write `count` staged output tiles (final core values) of head h, tiles
+// first, first + step, ..: each token's 256 bytes of the head go out as 16
+// coalesced 16-byte pieces; the whole workgroup shares the pieces.
 __device__ __forceinline__ void flush_tiles(const KArgs& a, int h, int first, int step, int count,
                                             uint8_t (*s_out)[LDS_OUT]) {
   for (int i = threadIdx.x; i < count * STORE_LANES; i += THREADS) {
@@ -349,9 +360,7 @@ __device__ __forceinline__ void flush_tiles(const KArgs& a, int h, int first, in
     const int t = (first + k * step) * TILE_T + tok;
     if (t >= a.S) continue;
     const int64_t off = ((int64_t)t * GROWS + h * VD + col) * 2;
-    const uint4 g8 = load_nt16(a.gate + off);
-    const uint4 av = *reinterpret_cast<const uint4*>(s_out[k] + tok * OUT_ROW + col * 2);
-    store_nt16(a.core + off, gate_mul(av, g8));
+    store_nt16(a.core + off, *reinterpret_cast<const uint4*>(s_out[k] + tok * OUT_ROW + col * 2));
   }
 }
 
@@ -365,7 +374,10 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
   __shared__ __attribute__((aligned(16))) uint8_t s_out[OUT_TILES][LDS_OUT];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (tokens, row bases)
+  // stays in scalar registers, and row loads take a scalar base plus the
+  // lane's 32-bit offset
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x % NH;      // this workgroup's head, fixed
   const int slot = blockIdx.x / NH;   // its token tiles: slot, slot + wg_per_head, ...
   const int ntiles = (a.S + TILE_T - 1) / TILE_T;
@@ -391,6 +403,11 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
     uint8_t* codes = s_codes[it & 1];
     uint8_t* scales = s_scales[it & 1];
     const int t0 = tile * TILE_T;
+    // the 4 gate values of this lane's outputs (token tl, rows v0..v0+3),
+    // loaded now so that their latency hides behind the merge
+    const int t_out = t0 + tl;
+    uint2 g4 = make_uint2(0u, 0u);
+    if (t_out < a.S) g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
 
     // ---- merge + quantise: wave owns tile slots 2 wave and 2 wave + 1
     const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
@@ -431,14 +448,18 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
     // lanes).
     asm volatile("" : "+v"(acc));
 
-    // ---- stage bf16(acc) ([mla_back: stage_uv]): the lane holds rows
-    // v0..v0+3 (v0 = 16 wave + 4 kb) of token tl. Tiles are kept in LDS and
-    // written (times the gate) when OUT_TILES have gathered or the
+    // ---- gate and stage ([mla_back: stage_uv]): the lane holds rows
+    // v0..v0+3 (v0 = 16 wave + 4 kb) of token tl. The finished core values
+    // are kept in LDS and written when OUT_TILES have gathered or the
     // workgroup's tiles are done: the writes then come in bursts, mostly
     // after the read stream, instead of competing with it all along.
+    // core = bf16( bf16(acc) * gate ): the product of two bf16 values is
+    // exact in float32, so that is one rounding
     const int slot_out = it % OUT_TILES;
+    const uint2 ab = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
     *reinterpret_cast<uint2*>(s_out[slot_out] + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
-        make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+        make_uint2(pack_bf16(bf_lo(ab.x) * bf_lo(g4.x), bf_hi(ab.x) * bf_hi(g4.x)),
+                   pack_bf16(bf_lo(ab.y) * bf_lo(g4.y), bf_hi(ab.y) * bf_hi(g4.y)));
     const bool last = tile + wg_per_head >= ntiles;
     if (slot_out == OUT_TILES - 1 || last) {
       __syncthreads();
@@ -467,7 +488,10 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
   __shared__ __attribute__((aligned(16))) uint8_t s_out[LDS_OUT];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (tokens, row bases)
+  // stays in scalar registers, and row loads take a scalar base plus the
+  // lane's 32-bit offset
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x % NH;
   const int tile = blockIdx.x / NH;
   const int t0 = tile * TILE_T;
