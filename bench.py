@@ -103,6 +103,37 @@ def time_gpu(call, steps: int, warmup: int, torch) -> dict:
     return {"wall_s": wall, "event_ms": ev0.elapsed_time(ev1)}
 
 
+def time_per_call(call, calls: int, torch, scratch=None) -> float:
+    """Median of HIP events around each single call (device synchronised
+    between calls). With `scratch` (a 1 GiB device tensor) the calls are cold:
+    the scratch is overwritten before each one, so the caches (L2, MALL) hold
+    none of the call's inputs; only the call itself is inside the events."""
+    import statistics
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(calls):
+        if scratch is not None:
+            scratch.fill_(1)
+        ev0.record()
+        call()
+        ev1.record()
+        torch.cuda.synchronize()
+        out.append(1e3 * ev0.elapsed_time(ev1))
+    return statistics.median(out)
+
+
+def copy_ceiling(torch) -> float:
+    """Device copy rate (GB/s, bytes read + bytes written) of a plain 1 GiB
+    copy: the stream-copy ceiling the kernel is also compared with."""
+    n = 1 << 29  # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    t = time_gpu(lambda: dst.copy_(src), 20, 3, torch)
+    return 2 * 2 * n * 20 / (t["event_ms"] * 1e-3) / 1e9
+
+
 def cpu_baseline(w, tokens: int) -> dict:
     """The oracle as it is, single-threaded (BLAS limited to one thread), on
     the first `tokens` tokens of the same workload; W_V encoded by the
@@ -139,6 +170,56 @@ def cpu_baseline(w, tokens: int) -> dict:
         "kind": "oracle",
         "sample": f"first {tokens} of {w.S} tokens of the same workload, in chunks of {chunk}, one thread "
         f"({dt:.1f} s; host {cpu}, {os.cpu_count()} logical CPUs)",
+    }
+
+
+_POOL_STATE = {}
+
+
+def _pool_init() -> None:
+    from threadpoolctl import threadpool_limits
+
+    _POOL_STATE["limit"] = threadpool_limits(limits=1)
+
+
+def _pool_chunk(bounds) -> int:
+    import numpy as np
+
+    import oracle.post as O
+
+    st = _POOL_STATE
+    s0, s1 = bounds
+    O.mla_post(st["o"], st["lse"], st["codes"], st["scales"], st["gate"], tokens=np.arange(s0, s1))
+    return s1 - s0
+
+
+def cpu_baseline_all_cores(w, tokens: int, workers: int) -> dict:
+    """The same oracle calls as cpu_baseline, spread over `workers` forked
+    processes (one BLAS thread each) by chunks of 64 tokens. Run before the
+    process touches the GPU, so the forked workers inherit no device state."""
+    import multiprocessing as mp
+
+    import oracle.post as O
+
+    codes, scales = O.quantize_mxfp4(w.wv_bits)
+    if "o_logical" in w.notes:
+        o, lse = w.notes["o_logical"], w.notes["lse_logical"]
+    else:
+        o, lse = w.o_view(), w.lse_view()
+    _POOL_STATE.update(o=o, lse=lse, codes=codes, scales=scales, gate=w.gate)
+    chunks = [(s0, min(tokens, s0 + 64)) for s0 in range(0, tokens, 64)]
+    with mp.get_context("fork").Pool(workers, initializer=_pool_init) as pool:
+        pool.map(_pool_chunk, chunks[:workers], chunksize=1)  # workers up, imports done (not timed)
+        t0 = time.perf_counter()
+        done = sum(pool.map(_pool_chunk, chunks, chunksize=1))
+        dt = time.perf_counter() - t0
+    _POOL_STATE.clear()
+    return {
+        "value": round(done / dt, 2),
+        "unit": "tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"first {tokens} of {w.S} tokens, chunks of 64 over {workers} processes ({dt:.2f} s)",
     }
 
 
@@ -224,6 +305,9 @@ def main() -> int:
     )
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample size (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument(
+        "--cpu-workers", type=int, default=0, help="processes for the all-cores oracle timing (default min(16, CPUs); 1 skips it)"
+    )
     ap.add_argument("--all", action="store_true", help="also time the four other standard workloads (stderr)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument(
@@ -250,18 +334,32 @@ def main() -> int:
     import mla_split_kv_amd as m
     import synth
 
-    if not torch.cuda.is_available():
+    # counting devices does not initialise the GPU; the oracle timings below
+    # fork worker processes, which must happen before anything touches it
+    if torch.cuda.device_count() < 1:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    torch.cuda.set_device(0)
-    m.load()
     if args.calibrate_copy:
+        torch.cuda.set_device(0)
+        m.load()
         calibrate_copy(torch)
         return 0
 
     log(f"generating the {args.workload} workload (seeded, 805 MB of partials)")
     w = synth.large_decode() if args.workload == "large_decode" else synth.EXTRA[args.workload]()
     alg = algorithmic_bytes(w)
+
+    cpu = cpu_all = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens, one thread")
+        cpu = cpu_baseline(w, args.cpu_tokens)
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        if workers > 1:
+            log(f"timing the CPU oracle on {args.cpu_tokens} tokens, {workers} processes")
+            cpu_all = cpu_baseline_all_cores(w, args.cpu_tokens, workers)
+
+    torch.cuda.set_device(0)
+    m.load()
     d = device_setup(w, m, torch)
     call = m.prepare(d["o"], d["lse"], d["w_v"], d["w_s"], d["gate"], d["core"], **layout_args(w))
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
@@ -271,8 +369,10 @@ def main() -> int:
     achieved = alg["alg_bytes"] / (kernel_us * 1e-6) / 1e9
     tokens_per_s = w.S * args.steps / t["wall_s"]
 
+    copy_gbps = copy_ceiling(torch)
     extra = {}
     if args.all:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB, for cold calls
         for name in ("tiny", "no_merge", "split_merge", "dcp8"):
             wk = synth.STANDARD[name]()
             dk = device_setup(wk, m, torch)
@@ -280,14 +380,36 @@ def main() -> int:
             tk = time_gpu(ck, 2000, 100, torch)
             ak = algorithmic_bytes(wk)
             us = 1e3 * tk["event_ms"] / 2000
-            extra[name] = {"us_per_call": round(us, 3), "GBps": round(ak["alg_bytes"] / (us * 1e-6) / 1e9, 1)}
+            gbps = ak["alg_bytes"] / (us * 1e-6) / 1e9
+            extra[name] = {
+                "us_per_call": round(us, 3),
+                "GBps": round(gbps, 1),
+                "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                "tokens_per_s": round(wk.S / (us * 1e-6), 1),
+                "us_single_warm": round(time_per_call(ck, 200, torch), 3),
+                "us_single_cold": round(time_per_call(ck, 100, torch, scratch), 3),
+                "alg_bytes": ak["alg_bytes"],
+            }
             log(f"{name}: {extra[name]}")
             del dk, ck
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(w, args.cpu_tokens)
+        del scratch
+        if args.workload == "large_decode":
+            wk = synth.EXTRA["large_decode_request_major"]()
+            dk = device_setup(wk, m, torch)
+            ck = m.prepare(dk["o"], dk["lse"], dk["w_v"], dk["w_s"], dk["gate"], dk["core"], **layout_args(wk))
+            tk = time_gpu(ck, args.steps, args.warmup, torch)
+            ak = algorithmic_bytes(wk)
+            us = 1e3 * tk["event_ms"] / args.steps
+            gbps = ak["alg_bytes"] / (us * 1e-6) / 1e9
+            extra["large_decode_request_major"] = {
+                "us_per_call": round(us, 3),
+                "GBps": round(gbps, 1),
+                "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                "tokens_per_s": round(wk.S / (us * 1e-6), 1),
+                "alg_bytes": ak["alg_bytes"],
+            }
+            log(f"large_decode_request_major: {extra['large_decode_request_major']}")
+            del dk, ck
 
     out = {
         "metric": "tokens/s and us per mla_post call; achieved HBM GB/s vs peak (1 GPU)",
@@ -328,7 +450,14 @@ def main() -> int:
             "traffic": traffic_entry(alg),
         },
         "cpu_baseline": cpu,
+        "copy_ceiling": {
+            "GBps": round(copy_gbps, 1),
+            "frac": round(achieved / copy_gbps, 4),
+            "what": "plain 1 GiB device copy, bytes read + written per second",
+        },
     }
+    if cpu_all:
+        out["cpu_baseline_all_cores"] = cpu_all
     if extra:
         out["other_workloads"] = extra
     log(f"host: {platform.node()} python {platform.python_version()} torch {torch.__version__}")
