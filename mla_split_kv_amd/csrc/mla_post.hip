@@ -98,16 +98,38 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
+// Lane permutations within each row of 16 lanes (DPP controls): swap
+// neighbours, swap pairs, mirror each half row, mirror the row. Applied in
+// that order with an associative operation, they leave every lane of a row
+// holding the row's reduction.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Max over the 64 lanes, as a wave-uniform value: within rows by DPP, then
+// the four rows' results combined from lanes 0, 16, 32 and 48.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<DPP_XOR1>(x));
+  x = fmaxf(x, dpp<DPP_XOR2>(x));
+  x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp<DPP_MIRROR>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+
+// Sum over the 64 lanes, as a wave-uniform value (same pattern as wave_max).
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  x += dpp<DPP_MIRROR>(x);
+  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
 }
 
 // LSE NaN / +inf -> -inf ([mla_back: sane]).
@@ -164,6 +186,35 @@ __device__ __forceinline__ void load_lse(const KArgs& a, int t, int r, int h, in
     }
     l[c] = x;
   }
+}
+
+// The LSEs and KV lengths of one (t, h) as they are stored, one per lane:
+// lane j of chunk c takes partial 64c + j. Every lane issues the same two
+// loads on every path (lanes past n re-read partial n - 1; without KV
+// lengths the second load re-reads the first LSE, and its value is ignored),
+// so the number of loads in flight is fixed and nothing waits for the values
+// here: finish_lse sanitises and masks them when they are used.
+template <int NCH>
+__device__ __forceinline__ void issue_lse(const KArgs& a, int t, int h, int lane, float x[NCH], int kv[NCH]) {
+  const int r = t / a.q;
+  const bool masked = a.kv_lens != nullptr;
+  const int32_t* kvp = masked ? a.kv_lens : reinterpret_cast<const int32_t*>(a.lse);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int j = min(64 * c + lane, a.n - 1);
+    x[c] = a.lse[(int64_t)j * a.l_sj + (int64_t)r * a.l_sr + (int64_t)t * a.l_st + (int64_t)h * a.l_sh];
+    kv[c] = kvp[masked ? (int64_t)j * a.kl_sj + r : 0];
+  }
+}
+
+// Raw LSEs from issue_lse -> the values load_lse gives: NaN / +inf -> -inf
+// ([mla_back: sane]), -inf past n and for partials whose request has no KV
+// ([mla_back: stage_push]).
+template <int NCH>
+__device__ __forceinline__ void finish_lse(const KArgs& a, int lane, float x[NCH], const int kv[NCH]) {
+  const bool masked = a.kv_lens != nullptr;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) x[c] = (64 * c + lane < a.n && !(masked && kv[c] == 0)) ? sane(x[c]) : -INFINITY;
 }
 
 // LSEs -> merge weights, in place ([mla_back: combine_splits],
@@ -328,16 +379,16 @@ __device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h
   quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
 }
 
-// Sanitised LSEs of this wave's two tokens of token tile `tile` (all -inf for
-// tokens past S or past the batch, or when the tile does not exist).
+// Raw LSEs of this wave's two tokens of token tile `tile` (issue_lse). The
+// loads are issued for every tile and token, the token index clamped to
+// S - 1, so that their number never varies; tokens past S or past the batch
+// and tiles that do not exist never use them.
 template <int NCH>
-__device__ __forceinline__ void prefetch_lse(const KArgs& a, int tile, int batch_end, int h, int wave, int lane,
-                                             float lA[NCH], float lB[NCH]) {
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) lA[c] = lB[c] = -INFINITY;
-  const int tA = tile * TILE_T + wave * TOK_PER_WAVE, tB = tA + 1;
-  if (tA < a.S && tA < batch_end) load_lse<NCH>(a, tA, tA / a.q, h, lane, lA);
-  if (tB < a.S && tB < batch_end) load_lse<NCH>(a, tB, tB / a.q, h, lane, lB);
+__device__ __forceinline__ void prefetch_lse(const KArgs& a, int tile, int h, int wave, int lane, float lA[NCH],
+                                             int kA[NCH], float lB[NCH], int kB[NCH]) {
+  const int tA = tile * TILE_T + wave * TOK_PER_WAVE;
+  issue_lse<NCH>(a, min(tA, a.S - 1), h, lane, lA, kA);
+  issue_lse<NCH>(a, min(tA + 1, a.S - 1), h, lane, lB, kB);
 }
 
 // 8 bf16 W_UV results times 8 bf16 gate values, each rounded once to bf16
@@ -393,22 +444,17 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
 
   // LSEs of this wave's two tokens, loaded one tile ahead: the next tile's
-  // loads are issued before this tile's barrier, MFMAs and stores, so their
-  // latency is hidden behind them.
+  // loads are issued before this tile's barrier, MFMAs and stores, and only
+  // used when the next tile starts, so their latency is hidden behind them.
   float lA[NCH], lB[NCH];
-  if constexpr (!NOLSE) prefetch_lse<NCH>(a, slot, batch_end, h, wave, lane, lA, lB);
+  int kA[NCH], kB[NCH];
+  if constexpr (!NOLSE) prefetch_lse<NCH>(a, slot, h, wave, lane, lA, kA, lB, kB);
 
 #pragma unroll 1
   for (int tile = slot, it = 0; tile < ntiles; tile += wg_per_head, ++it) {
     uint8_t* codes = s_codes[it & 1];
     uint8_t* scales = s_scales[it & 1];
     const int t0 = tile * TILE_T;
-    // the 4 gate values of this lane's outputs (token tl, rows v0..v0+3),
-    // loaded now so that their latency hides behind the merge
-    const int t_out = t0 + tl;
-    uint2 g4 = make_uint2(0u, 0u);
-    if (t_out < a.S) g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
-
     // ---- merge + quantise: wave owns tile slots 2 wave and 2 wave + 1
     const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
     const int tA = t0 + ttA, tB = t0 + ttB;
@@ -421,12 +467,23 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
         wA[c] = lA[c];
         wB[c] = lB[c];
       }
-      if (liveA && !emptyA) lse_to_weights<NCH>(wA);
-      if (liveB && !emptyB) lse_to_weights<NCH>(wB);
+      if (liveA && !emptyA) {
+        finish_lse<NCH>(a, lane, wA, kA);
+        lse_to_weights<NCH>(wA);
+      }
+      if (liveB && !emptyB) {
+        finish_lse<NCH>(a, lane, wB, kB);
+        lse_to_weights<NCH>(wB);
+      }
     }
+    // the 4 gate values of this lane's outputs (token tl, rows v0..v0+3),
+    // loaded now so that their latency hides behind the merge; a token past
+    // S re-reads row S - 1 (its output is never stored)
+    const int t_out = min(t0 + tl, a.S - 1);
+    const uint2 g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
     token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, emptyA, wA, codes, scales);
     token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, emptyB, wB, codes, scales);
-    if constexpr (!NOLSE) prefetch_lse<NCH>(a, tile + wg_per_head, batch_end, h, wave, lane, lA, lB);
+    if constexpr (!NOLSE) prefetch_lse<NCH>(a, tile + wg_per_head, h, wave, lane, lA, kA, lB, kB);
     // One barrier per tile: it publishes this tile's codes, and since every
     // wave finished the previous tile's MFMAs before merging this one, the
     // other buffer is free for the next tile.
