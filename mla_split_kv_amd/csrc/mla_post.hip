@@ -9,11 +9,13 @@
 // Decomposition (this library's own, not the page's):
 //   workgroup = 8 waves of 64 lanes that own one head h for the whole launch
 //     and walk its 16-token tiles (k workgroups per head, k filling the
-//     device once); W_V[h]'s operands stay in registers throughout;
+//     device once); W_V[h]'s operands are re-read from L2 for each tile
+//     (after the merge, so they hold no registers during the row stream);
 //   merge: per tile, wave w owns tokens 2w and 2w+1; a token's partial row
 //     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced non-temporal
 //     16-byte load per lane, ROWS_IN_FLIGHT rows in flight, rows of weight 0
 //     not loaded; the next tile's LSEs are loaded a tile ahead;
+//     the DPP in-row reductions give the weights without LDS traffic;
 //   the merged latents never go to memory: each lane rounds its 8 latents
 //     to bf16, the 4 lanes of a 32-element block agree on the E8M0 code with
 //     two DPP steps, and the hardware scaled convert packs the 8 FP4 codes;
@@ -21,9 +23,9 @@
 //   W_UV: wave w multiplies W_V[h] rows 16w..16w+15 (A operand) by the 16
 //     tokens' latent codes, four 16x16x128 scaled FP4 MFMAs over K = 512, so
 //     all 16 MFMA columns carry live tokens (the page fills 4 of 16);
-//   epilogue: bf16(acc) tiles are held in LDS and written when the
-//     workgroup's tiles are done: x gate -> bf16, 16-byte non-temporal
-//     stores, tokens < S only.
+//   epilogue: bf16(acc) x gate -> bf16 tiles are held in LDS and written
+//     when the workgroup's tiles are done: 16-byte non-temporal stores,
+//     tokens < S only.
 
 #include <hip/hip_runtime.h>
 
@@ -47,7 +49,7 @@ constexpr int THREADS = WAVES * 64;            // 512
 constexpr int TOK_PER_WAVE = TILE_T / WAVES;   // 2
 constexpr int ROWS_IN_FLIGHT = 8;              // partial rows a wave loads before it sums
 constexpr bool NT_ROWS = true;                 // partial rows loaded non-temporally
-constexpr int WG_PER_CU = 3;                   // resident workgroups per CU at this register budget
+constexpr int WG_PER_CU = 3;                   // resident workgroups per CU (80 registers, 44 KiB LDS)
 #ifndef MLA_KERNEL_ATTRS
 #define MLA_KERNEL_ATTRS
 #endif
@@ -319,15 +321,23 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, const uint8_t* rowbas
 // W_V[h] rows wave*16 + tl, K block kb of each of the 4 K steps
 // ([mla_back: wv_loads]); the four scale bytes packed into one word, byte st
 // for K step st.
-__device__ __forceinline__ void load_wv(const KArgs& a, int h, int wave, int tl, int kb, uint4 wv[4], int& sa) {
-  const int v = wave * 16 + tl;
-  const uint8_t* wrow = a.w_v + h * a.w_sh + v * a.w_sv + kb * 16;
+__device__ __forceinline__ void load_wv_codes(const KArgs& a, int h, int wave, int tl, int kb, uint4 wv[4]) {
+  const uint8_t* wrow = a.w_v + h * a.w_sh + (wave * 16 + tl) * a.w_sv + kb * 16;
 #pragma unroll
   for (int st = 0; st < 4; ++st) wv[st] = *reinterpret_cast<const uint4*>(wrow + st * 64);
-  const uint8_t* srow = a.w_vs + h * a.s_sh + v * a.s_sv;
-  sa = 0;
+}
+
+__device__ __forceinline__ int load_wv_scales(const KArgs& a, int h, int wave, int tl, int kb) {
+  const uint8_t* srow = a.w_vs + h * a.s_sh + (wave * 16 + tl) * a.s_sv;
+  int sa = 0;
 #pragma unroll
   for (int st = 0; st < 4; ++st) sa |= (int)srow[(st * 4 + kb) * a.s_sb] << (8 * st);
+  return sa;
+}
+
+__device__ __forceinline__ void load_wv(const KArgs& a, int h, int wave, int tl, int kb, uint4 wv[4], int& sa) {
+  load_wv_codes(a, h, wave, tl, kb, wv);
+  sa = load_wv_scales(a, h, wave, tl, kb);
 }
 
 // bf16 latents of token t (tile slot tt) -> MXFP4 codes and scale into LDS
@@ -417,8 +427,31 @@ __device__ __forceinline__ void flush_tiles(const KArgs& a, int h, int first, in
 
 // ---------------------------------------------------------------- the fused kernel
 
+// The device deals workgroups to its 8 XCDs in turn (workgroup i to XCD
+// i mod 8), each XCD with its own L2. When the grid is a multiple of 8 x 12,
+// the 12 heads of one token-tile slot go to consecutive workgroups of one
+// XCD, so they run at the same time behind the same L2: the LSE lines they
+// share are fetched once, and the 12 pieces of each core row are written
+// together. Otherwise workgroup i takes head i mod 12 and slot i / 12. Either
+// way the map is one to one onto (head, slot).
+constexpr int XCDS = 8;
+
+__device__ __forceinline__ void head_and_slot(int& h, int& slot) {
+  if (gridDim.x % (XCDS * NH) == 0) {
+    const int xcd = blockIdx.x % XCDS, k = blockIdx.x / XCDS;
+    h = k % NH;
+    slot = xcd + XCDS * (k / NH);
+  } else {
+    h = blockIdx.x % NH;
+    slot = blockIdx.x / NH;
+  }
+}
+
+// With at most 64 partials, 6 waves per SIMD (80 registers) keep WG_PER_CU
+// workgroups resident on every CU, so the whole grid runs in one round.
 template <bool NOLSE, int NCH>
-__global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(NCH == 1 ? 6 : 1)))
+MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
   // two LDS buffers: a wave may merge tile i+1 while others still read tile i
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][LDS_SCALES];
@@ -429,17 +462,16 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
   // stays in scalar registers, and row loads take a scalar base plus the
   // lane's 32-bit offset
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.x % NH;      // this workgroup's head, fixed
-  const int slot = blockIdx.x / NH;   // its token tiles: slot, slot + wg_per_head, ...
+  int h, slot;  // this workgroup's head, fixed, and its token tiles slot, slot + wg_per_head, ...
+  head_and_slot(h, slot);
   const int ntiles = (a.S + TILE_T - 1) / TILE_T;
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
-  // W_V[h]'s operands for this wave's 16 rows stay in registers for every
-  // tile of the head.
+  // W_V[h]'s A operands for this wave's 16 rows (read per tile) and their
+  // scale codes (read once).
   uint4 wv[4];
-  int sa = 0;
-  load_wv(a, h, wave, tl, kb, wv, sa);
+  const int sa = load_wv_scales(a, h, wave, tl, kb);
   // tokens at or past qsl[R] lie past the batch: every partial is empty
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
 
@@ -483,6 +515,11 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
     const uint2 g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
     token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, emptyA, wA, codes, scales);
     token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, emptyB, wB, codes, scales);
+    // W_V[h] is 34 KiB per head and stays in L2 (the partial rows, loaded
+    // non-temporally, do not evict it): re-reading the A operands here,
+    // after the merge, keeps their 16 registers free during the row stream,
+    // which is what lets WG_PER_CU workgroups fit on a CU
+    load_wv_codes(a, h, wave, tl, kb, wv);
     if constexpr (!NOLSE) prefetch_lse<NCH>(a, tile + wg_per_head, h, wave, lane, lA, kA, lB, kB);
     // One barrier per tile: it publishes this tile's codes, and since every
     // wave finished the previous tile's MFMAs before merging this one, the
