@@ -9,13 +9,14 @@
 // Decomposition (this library's own, not the page's):
 //   workgroup = 8 waves of 64 lanes that own one head h for the whole launch
 //     and walk its 16-token tiles (k workgroups per head, k filling the
-//     device once); W_V[h]'s operands are re-read from L2 for each tile
-//     (after the merge, so they hold no registers during the row stream);
+//     device once); W_V[h]'s operands stay in registers throughout;
 //   merge: per tile, wave w owns tokens 2w and 2w+1; a token's partial row
 //     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced non-temporal
 //     16-byte load per lane, ROWS_IN_FLIGHT rows in flight, rows of weight 0
-//     not loaded; the next tile's LSEs are loaded a tile ahead;
-//     the DPP in-row reductions give the weights without LDS traffic;
+//     not loaded; software-pipelined over tiles: before the barrier of a
+//     tile a wave computes the next tile's weights (LSEs loaded a tile
+//     earlier, DPP reductions) and issues that tile's first rows, so it
+//     keeps loads in flight through the barrier and the MFMAs;
 //   the merged latents never go to memory: each lane rounds its 8 latents
 //     to bf16, the 4 lanes of a 32-element block agree on the E8M0 code with
 //     two DPP steps, and the hardware scaled convert packs the 8 FP4 codes;
@@ -48,8 +49,9 @@ constexpr int WAVES = VD / 16;                 // 8 waves x 16 W_V rows
 constexpr int THREADS = WAVES * 64;            // 512
 constexpr int TOK_PER_WAVE = TILE_T / WAVES;   // 2
 constexpr int ROWS_IN_FLIGHT = 8;              // partial rows a wave loads before it sums
+constexpr int PF_ROWS = ROWS_IN_FLIGHT;        // first rows of the next tile issued before the barrier
 constexpr bool NT_ROWS = true;                 // partial rows loaded non-temporally
-constexpr int WG_PER_CU = 3;                   // resident workgroups per CU (80 registers, 44 KiB LDS)
+constexpr int WG_PER_CU = 3;                   // workgroups per CU in the grid (2 resident at a time)
 #ifndef MLA_KERNEL_ATTRS
 #define MLA_KERNEL_ATTRS
 #endif
@@ -291,29 +293,49 @@ __device__ __forceinline__ void fma_row(float w, const uint4& v, float acc[8]) {
   acc[7] = fmaf(w, bf_hi(v.w), acc[7]);
 }
 
-// Weighted sum of the partial rows of (t, h) for this lane's 8 latents
-// [k = 8 lane .. 8 lane + 7], skipping rows of weight 0 (not even loaded).
-template <int NCH>
-__device__ __forceinline__ void merge_rows(const KArgs& a, const uint8_t* rowbase, int lane, const float wts[NCH],
-                                           float acc[8]) {
+// Rows j0 .. j0 + R - 1 of chunk c of one (t, h): one 16-byte piece per lane
+// each, and their wave-uniform weights. A row of weight 0, or past n, is
+// loaded through a buffer resource of zero bytes, which returns zeros without
+// touching memory, so every call issues exactly R loads: the number of loads
+// in flight never depends on the data, and later waits (the gate, W_V) can
+// leave them in flight.
+template <int R>
+__device__ __forceinline__ void issue_rows(const KArgs& a, const uint8_t* rowbase, int lane, int wbits, int c, int j0,
+                                           uint4 v[R], float w[R]) {
+  const int nc = min(64, a.n - 64 * c);
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+    const int jl = j0 + b;
+    int wb = __builtin_amdgcn_readlane(wbits, jl & 63);
+    if (jl >= nc) wb = 0;
+    w[b] = __int_as_float(wb);
+    const uint8_t* p = rowbase + (int64_t)(64 * c + min(jl, nc - 1)) * a.o_sj;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p), (short)0, (wb & 0x7FFFFFFF) ? KVL * 2 : 0, BUF_WORD3);
+    const v4u t = (v4u)__builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, NT_ROWS ? 2 : 0);  // 2: nt
+    v[b] = make_uint4(t.x, t.y, t.z, t.w);
+  }
+}
+
+// acc += the weighted rows of one (t, h), in the order j = 0, 1, .., n - 1;
+// with PRE the first PF_ROWS rows of chunk 0 are already in flight (pv, pw).
+template <int NCH, bool PRE>
+__device__ __forceinline__ void merge_token(const KArgs& a, const uint8_t* rowbase, int lane, const float wts[NCH],
+                                            const uint4 pv[PF_ROWS], const float pw[PF_ROWS], float acc[8]) {
+  if constexpr (PRE) {
+#pragma unroll
+    for (int b = 0; b < PF_ROWS; ++b) fma_row(pw[b], pv[b], acc);
+  }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int nc = min(64, a.n - 64 * c);
     const int wbits = __float_as_int(wts[c]);
-    for (int j0 = 0; j0 < nc; j0 += ROWS_IN_FLIGHT) {
+    for (int j0 = (PRE && c == 0) ? PF_ROWS : 0; j0 < nc; j0 += ROWS_IN_FLIGHT) {
       uint4 v[ROWS_IN_FLIGHT];
-      float wj[ROWS_IN_FLIGHT];
+      float w[ROWS_IN_FLIGHT];
+      issue_rows<ROWS_IN_FLIGHT>(a, rowbase, lane, wbits, c, j0, v, w);
 #pragma unroll
-      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) {
-        const int jl = j0 + b;
-        int wb = __builtin_amdgcn_readlane(wbits, jl & 63);
-        if (jl >= nc) wb = 0;
-        wj[b] = __int_as_float(wb);
-        v[b] = make_uint4(0, 0, 0, 0);
-        if (wb & 0x7FFFFFFF) v[b] = load_row16(rowbase + (int64_t)(64 * c + jl) * a.o_sj, lane);
-      }
-#pragma unroll
-      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) fma_row(wj[b], v[b], acc);
+      for (int b = 0; b < ROWS_IN_FLIGHT; ++b) fma_row(w[b], v[b], acc);
     }
   }
 }
@@ -363,28 +385,31 @@ __device__ __forceinline__ const uint8_t* row_base(const KArgs& a, int t, int h)
   return a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (int64_t)(t / a.q) * a.o_sr;
 }
 
-// Latents of token t (tile slot tt) -> bf16 -> MXFP4 into LDS.
-// `empty`: every partial of token t is masked (past the batch), so the
-// latents are +0 without reading anything.
-template <bool NOLSE, int NCH>
-__device__ __forceinline__ void token_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
-                                            const float wts[NCH], uint8_t* s_codes, uint8_t* s_scales) {
+// One partial and no LSE: token t's row (tile slot tt) is the attention
+// output itself, used as the bf16 latents unless its request is masked as
+// having no KV or the token lies past the batch (`empty`); -> MXFP4 into LDS.
+__device__ __forceinline__ void copy_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
+                                           uint8_t* s_codes, uint8_t* s_scales) {
+  uint32_t lat[4] = {0u, 0u, 0u, 0u};
+  if (live && !empty && !(a.kv_lens && a.kv_lens[t / a.q] == 0)) {
+    const uint4 v = load_row16(row_base(a, t, h), lane);
+    lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+  }
+  quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
+}
+
+// Token t (tile slot tt) of the persistent kernel with LSEs: merged latents
+// -> bf16 -> MXFP4 into LDS. With PRE its first PF_ROWS rows are in flight.
+template <int NCH, bool PRE>
+__device__ __forceinline__ void merge_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
+                                            const float wts[NCH], const uint4 pv[PF_ROWS], const float pw[PF_ROWS],
+                                            uint8_t* s_codes, uint8_t* s_scales) {
   uint32_t lat[4] = {0u, 0u, 0u, 0u};
   if (live && !empty) {
-    const uint8_t* rowbase = row_base(a, t, h);
-    if constexpr (NOLSE) {
-      // one partial and no LSE: the row is the attention output itself
-      // (unless its request is masked as having no KV)
-      if (!(a.kv_lens && a.kv_lens[t / a.q] == 0)) {
-        const uint4 v = load_row16(rowbase, lane);
-        lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
-      }
-    } else {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      merge_rows<NCH>(a, rowbase, lane, wts, acc);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    merge_token<NCH, PRE>(a, row_base(a, t, h), lane, wts, pv, pw, acc);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
-    }
+    for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
   }
   quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
 }
@@ -399,6 +424,45 @@ __device__ __forceinline__ void prefetch_lse(const KArgs& a, int tile, int h, in
   const int tA = tile * TILE_T + wave * TOK_PER_WAVE;
   issue_lse<NCH>(a, min(tA, a.S - 1), h, lane, lA, kA);
   issue_lse<NCH>(a, min(tA + 1, a.S - 1), h, lane, lB, kB);
+}
+
+// Merge weights of this wave's two tokens of token tile `tile` from their
+// raw LSEs (loaded a tile earlier); all zero for tokens past S or past the
+// batch, and for tiles that do not exist.
+template <int NCH>
+__device__ __forceinline__ void tile_weights(const KArgs& a, int tile, int batch_end, int wave, int lane,
+                                             const float lA[NCH], const int kA[NCH], const float lB[NCH],
+                                             const int kB[NCH], float wA[NCH], float wB[NCH]) {
+  const int tA = tile * TILE_T + wave * TOK_PER_WAVE, tB = tA + 1;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    wA[c] = lA[c];
+    wB[c] = lB[c];
+  }
+  if (tA < a.S && tA < batch_end) {
+    finish_lse<NCH>(a, lane, wA, kA);
+    lse_to_weights<NCH>(wA);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) wA[c] = 0.f;
+  }
+  if (tB < a.S && tB < batch_end) {
+    finish_lse<NCH>(a, lane, wB, kB);
+    lse_to_weights<NCH>(wB);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) wB[c] = 0.f;
+  }
+}
+
+// The first PF_ROWS rows of this wave's first token of tile `tile` (weights
+// wA), issued early; a token that does not exist has weights 0, so nothing
+// is read for it.
+template <int NCH>
+__device__ __forceinline__ void issue_first_rows(const KArgs& a, int tile, int h, int wave, int lane,
+                                                 const float wA[NCH], uint4 pv[PF_ROWS], float pw[PF_ROWS]) {
+  const int tA = min(tile * TILE_T + wave * TOK_PER_WAVE, a.S - 1);
+  issue_rows<PF_ROWS>(a, row_base(a, tA, h), lane, __float_as_int(wA[0]), 0, 0, pv, pw);
 }
 
 // 8 bf16 W_UV results times 8 bf16 gate values, each rounded once to bf16
@@ -447,11 +511,8 @@ __device__ __forceinline__ void head_and_slot(int& h, int& slot) {
   }
 }
 
-// With at most 64 partials, 6 waves per SIMD (80 registers) keep WG_PER_CU
-// workgroups resident on every CU, so the whole grid runs in one round.
 template <bool NOLSE, int NCH>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(NCH == 1 ? 6 : 1)))
-MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
+__global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
   // two LDS buffers: a wave may merge tile i+1 while others still read tile i
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][LDS_SCALES];
@@ -468,19 +529,29 @@ MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
-  // W_V[h]'s A operands for this wave's 16 rows (read per tile) and their
-  // scale codes (read once).
+  // W_V[h]'s operands for this wave's 16 rows stay in registers for every
+  // tile of the head.
   uint4 wv[4];
-  const int sa = load_wv_scales(a, h, wave, tl, kb);
+  int sa = 0;
+  load_wv(a, h, wave, tl, kb, wv, sa);
   // tokens at or past qsl[R] lie past the batch: every partial is empty
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
 
-  // LSEs of this wave's two tokens, loaded one tile ahead: the next tile's
-  // loads are issued before this tile's barrier, MFMAs and stores, and only
-  // used when the next tile starts, so their latency is hidden behind them.
-  float lA[NCH], lB[NCH];
+  // Software pipeline over the workgroup's tiles, so that a wave keeps loads
+  // in flight while it waits at the barrier and runs the MFMAs: before the
+  // barrier of tile i it turns tile i+1's LSEs (loaded during tile i-1) into
+  // weights, issues tile i+2's LSE loads and tile i+1's first PF_ROWS rows.
+  float lA[NCH], lB[NCH];  // raw LSEs of the next tile
   int kA[NCH], kB[NCH];
-  if constexpr (!NOLSE) prefetch_lse<NCH>(a, slot, h, wave, lane, lA, kA, lB, kB);
+  float wA[NCH], wB[NCH];  // weights of the current tile
+  uint4 pv[PF_ROWS];       // its first rows, in flight
+  float pw[PF_ROWS];
+  if constexpr (!NOLSE) {
+    prefetch_lse<NCH>(a, slot, h, wave, lane, lA, kA, lB, kB);
+    tile_weights<NCH>(a, slot, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
+    prefetch_lse<NCH>(a, slot + wg_per_head, h, wave, lane, lA, kA, lB, kB);
+    issue_first_rows<NCH>(a, slot, h, wave, lane, wA, pv, pw);
+  }
 
 #pragma unroll 1
   for (int tile = slot, it = 0; tile < ntiles; tile += wg_per_head, ++it) {
@@ -492,35 +563,24 @@ MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
     const int tA = t0 + ttA, tB = t0 + ttB;
     const bool liveA = tA < a.S, liveB = tB < a.S;
     const bool emptyA = tA >= batch_end, emptyB = tB >= batch_end;
-    float wA[NCH], wB[NCH];
-    if constexpr (!NOLSE) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        wA[c] = lA[c];
-        wB[c] = lB[c];
-      }
-      if (liveA && !emptyA) {
-        finish_lse<NCH>(a, lane, wA, kA);
-        lse_to_weights<NCH>(wA);
-      }
-      if (liveB && !emptyB) {
-        finish_lse<NCH>(a, lane, wB, kB);
-        lse_to_weights<NCH>(wB);
-      }
-    }
     // the 4 gate values of this lane's outputs (token tl, rows v0..v0+3),
     // loaded now so that their latency hides behind the merge; a token past
     // S re-reads row S - 1 (its output is never stored)
     const int t_out = min(t0 + tl, a.S - 1);
     const uint2 g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
-    token_stage<NOLSE, NCH>(a, tA, ttA, h, lane, liveA, emptyA, wA, codes, scales);
-    token_stage<NOLSE, NCH>(a, tB, ttB, h, lane, liveB, emptyB, wB, codes, scales);
-    // W_V[h] is 34 KiB per head and stays in L2 (the partial rows, loaded
-    // non-temporally, do not evict it): re-reading the A operands here,
-    // after the merge, keeps their 16 registers free during the row stream,
-    // which is what lets WG_PER_CU workgroups fit on a CU
-    load_wv_codes(a, h, wave, tl, kb, wv);
-    if constexpr (!NOLSE) prefetch_lse<NCH>(a, tile + wg_per_head, h, wave, lane, lA, kA, lB, kB);
+    if constexpr (NOLSE) {
+      copy_stage(a, tA, ttA, h, lane, liveA, emptyA, codes, scales);
+      copy_stage(a, tB, ttB, h, lane, liveB, emptyB, codes, scales);
+    } else {
+      merge_stage<NCH, true>(a, tA, ttA, h, lane, liveA, emptyA, wA, pv, pw, codes, scales);
+      merge_stage<NCH, false>(a, tB, ttB, h, lane, liveB, emptyB, wB, pv, pw, codes, scales);
+    }
+    if constexpr (!NOLSE) {
+      const int next = tile + wg_per_head;
+      tile_weights<NCH>(a, next, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
+      prefetch_lse<NCH>(a, next + wg_per_head, h, wave, lane, lA, kA, lB, kB);
+      issue_first_rows<NCH>(a, next, h, wave, lane, wA, pv, pw);
+    }
     // One barrier per tile: it publishes this tile's codes, and since every
     // wave finished the previous tile's MFMAs before merging this one, the
     // other buffer is free for the next tile.
