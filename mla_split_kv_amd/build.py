@@ -1,10 +1,12 @@
-"""Build libmla_post.so in-tree with hipcc for gfx950.
+"""Build libmla_post.so in-tree with hipcc for gfx950, and the C test client.
 
     python -m mla_split_kv_amd.build
 
 Compiles every time it is called (the C-ABI library, its kernels and host code
 from csrc/mla_post.hip). Packed-FP32 instructions are disabled for the device
 code; hipcc's host pass warns that it does not know that feature, harmlessly.
+build_c_client compiles tests/c/c_client.c, a plain C program that calls the
+library through the HIP runtime's C API, with gcc against include/ alone.
 """
 
 from __future__ import annotations
@@ -20,6 +22,9 @@ SRC = os.path.join(PKG, "csrc", "mla_post.hip")
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_post.so")
 ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c", "c_client")
 
 
 def hipcc() -> str:
@@ -59,5 +64,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_c_client() -> str:
+    """gcc, C99, warnings as errors; linked to the in-tree library by a
+    path relative to the executable, so the tree can move."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        raise RuntimeError("gcc not found")
+    tmp = C_CLIENT + ".tmp"
+    cmd = [
+        gcc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror",
+        "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-I", INC,
+        C_CLIENT_SRC, "-o", tmp,
+        "-L", PKG, "-lmla_post", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+        "-Wl,-rpath,$ORIGIN/../../mla_split_kv_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+    ]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed ({r.returncode}):\n{r.stdout}{r.stderr}")
+    os.replace(tmp, C_CLIENT)
+    return C_CLIENT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_client())
