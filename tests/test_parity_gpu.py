@@ -89,6 +89,38 @@ def test_large_decode_sampled(gpu_lib):
     say(f"{w.name}: sampled {len(tokens)} tokens {st}")
 
 
+@pytest.mark.parametrize(
+    "make",
+    [
+        # a second 64-lane LSE chunk holding 2 splits
+        pytest.param(lambda: synth.dense_splits("persistent_n66", 66, 1040, seed=25, p_neg_inf=0.2), id="n66_S1040"),
+        # decode-context-parallel gathered partials, 8 ranks, padded head stride
+        pytest.param(lambda: synth.dcp_gathered("persistent_dcp8", 8, 1100, seed=26, head_stride_rows=104, dead_from=1090),
+                     id="dcp8_S1100"),
+    ],
+)
+def test_persistent_multi_tile_sampled(gpu_lib, make):
+    """The persistent kernel with several token tiles per workgroup (S past
+    1024, so tiles i and i + 64 share a workgroup and the software pipeline
+    runs across them) and a ragged last tile: T2 on every block, T1, T3, T4
+    on tokens at tile and workgroup boundaries and a random sample."""
+    m = gpu_lib
+    w = make()
+    say(f"{w.name}: n={w.n} S={w.S}")
+    d = device_inputs(w)
+    g = run_debug(m, d)
+    C.check_t2(g["lat"], g["codes"], g["scales"])
+    rng = np.random.default_rng(9)
+    edges = [0, 1, 15, 16, 17, 1007, 1023, 1024, 1025, w.S - 2, w.S - 1]
+    tokens = np.unique(np.concatenate([edges, rng.integers(0, w.S, size=29)]))
+    ref = O.mla_post(w.o_view(), w.lse_view(), d["w_codes"], d["w_scales"], w.gate, tokens=tokens)
+    st = {}
+    st.update(C.check_t1(g["lat"][tokens], ref))
+    st.update(C.check_t3(g["core"][tokens], g["codes"][tokens], g["scales"][tokens], d["w_codes"], d["w_scales"], w.gate[tokens]))
+    st.update(C.check_t4(g["core"][tokens], ref, g["lat"][tokens], g["codes"][tokens], g["scales"][tokens]))
+    say(f"{w.name}: sampled {len(tokens)} tokens {st}")
+
+
 # ---------------------------------------------------------------- edge cases
 
 
