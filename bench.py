@@ -223,14 +223,14 @@ def cpu_baseline_all_cores(w, tokens: int, workers: int) -> dict:
     }
 
 
-def traffic_entry(alg: dict):
+def traffic_entry(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source."""
+    taken on this workload and on the current kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_sha():
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_sha():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -261,6 +261,7 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
     write = wk * 1024 * w_scale
     out = {
         "kernel": "mla_post_kernel<false, 1> (large decode workload)",
+        "workload": "large_decode",
         "kernel_source_sha256": kernel_sha(),
         "fetch_kib_per_dispatch": fk,
         "write_kib_per_dispatch": wk,
@@ -447,7 +448,7 @@ def main() -> int:
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_entry(alg),
+            "traffic": traffic_entry(args.workload),
         },
         "cpu_baseline": cpu,
         "copy_ceiling": {
