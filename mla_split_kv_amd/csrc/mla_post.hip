@@ -174,24 +174,6 @@ __device__ __forceinline__ v4f mfma_step(const uint4& a, const uint4& b, v4f acc
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, ST, sa, ST, sb);
 }
 
-// Sanitised LSEs of one (t, h): lane j of chunk c holds lse_{64c + j}, -inf
-// past n ([mla_back: sane]).
-// Push-side masking ([mla_back: stage_push]): a partial whose request r has
-// no KV in it (kv_lens[j, r] == 0) counts as LSE -inf.
-template <int NCH>
-__device__ __forceinline__ void load_lse(const KArgs& a, int t, int r, int h, int lane, float l[NCH]) {
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int j = 64 * c + lane;
-    float x = -INFINITY;
-    if (j < a.n) {
-      x = sane(a.lse[(int64_t)j * a.l_sj + (int64_t)r * a.l_sr + (int64_t)t * a.l_st + (int64_t)h * a.l_sh]);
-      if (a.kv_lens && a.kv_lens[(int64_t)j * a.kl_sj + r] == 0) x = -INFINITY;
-    }
-    l[c] = x;
-  }
-}
-
 // The LSEs and KV lengths of one (t, h) as they are stored, one per lane:
 // lane j of chunk c takes partial 64c + j. Every lane issues the same two
 // loads on every path (lanes past n re-read partial n - 1; without KV
@@ -211,7 +193,7 @@ __device__ __forceinline__ void issue_lse(const KArgs& a, int t, int h, int lane
   }
 }
 
-// Raw LSEs from issue_lse -> the values load_lse gives: NaN / +inf -> -inf
+// Raw LSEs from issue_lse -> sanitised and masked: NaN / +inf -> -inf
 // ([mla_back: sane]), -inf past n and for partials whose request has no KV
 // ([mla_back: stage_push]).
 template <int NCH>
@@ -679,9 +661,11 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
       latB[0] = v.x; latB[1] = v.y; latB[2] = v.z; latB[3] = v.w;
     }
   } else {
+    // LSE loads first, then every row, and only then anything that waits
     float lA[1] = {-INFINITY}, lB[1] = {-INFINITY};
-    if (useA) load_lse<1>(a, tA, tA / a.q, h, lane, lA);
-    if (useB) load_lse<1>(a, tB, tB / a.q, h, lane, lB);
+    int kA[1] = {1}, kB[1] = {1};
+    if (useA) issue_lse<1>(a, tA, h, lane, lA, kA);
+    if (useB) issue_lse<1>(a, tB, h, lane, lB, kB);
     uint4 rA[LAT_NMAX], rB[LAT_NMAX];
     const uint8_t* baseA = row_base(a, tA, h);
     const uint8_t* baseB = row_base(a, tB, h);
@@ -691,8 +675,14 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
       if (useA && j < a.n) rA[j] = load_row16(baseA + (int64_t)j * a.o_sj, lane);
       if (useB && j < a.n) rB[j] = load_row16(baseB + (int64_t)j * a.o_sj, lane);
     }
-    if (useA) lse_to_weights<1>(lA);
-    if (useB) lse_to_weights<1>(lB);
+    if (useA) {
+      finish_lse<1>(a, lane, lA, kA);
+      lse_to_weights<1>(lA);
+    }
+    if (useB) {
+      finish_lse<1>(a, lane, lB, kB);
+      lse_to_weights<1>(lB);
+    }
     float accA[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float accB[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
