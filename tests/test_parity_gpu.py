@@ -97,6 +97,9 @@ def test_large_decode_sampled(gpu_lib):
         # decode-context-parallel gathered partials, 8 ranks, padded head stride
         pytest.param(lambda: synth.dcp_gathered("persistent_dcp8", 8, 1100, seed=26, head_stride_rows=104, dead_from=1090),
                      id="dcp8_S1100"),
+        # more than 8 tiles per workgroup (S > 8 x 64 x 16): the staged output
+        # is written after 8 tiles and its buffers reused for the rest
+        pytest.param(lambda: synth.dense_splits("persistent_long", 2, 9000, seed=27, p_neg_inf=0.1), id="n2_S9000"),
     ],
 )
 def test_persistent_multi_tile_sampled(gpu_lib, make):
@@ -110,8 +113,17 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
     d = device_inputs(w)
     g = run_debug(m, d)
     C.check_t2(g["lat"], g["codes"], g["scales"])
+    # every row is written: a NaN-filled core comes back finite and equal to
+    # the first call's, bit for bit
+    core = torch.full((w.S, 1536), float("nan"), dtype=torch.bfloat16, device="cuda")
+    m.mla_post(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], core, **d["layout"])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(core), g["core"])
+    assert bool(torch.isfinite(core.float()).all())
     rng = np.random.default_rng(9)
     edges = [0, 1, 15, 16, 17, 1007, 1023, 1024, 1025, w.S - 2, w.S - 1]
+    if w.S > 8192:  # the first tile after a mid-kernel flush, and around it
+        edges += [8 * 1024 - 1, 8 * 1024, 8 * 1024 + 15, 8 * 1024 + 16]
     tokens = np.unique(np.concatenate([edges, rng.integers(0, w.S, size=29)]))
     ref = O.mla_post(w.o_view(), w.lse_view(), d["w_codes"], d["w_scales"], w.gate, tokens=tokens)
     st = {}
