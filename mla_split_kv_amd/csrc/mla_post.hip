@@ -617,7 +617,11 @@ __global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(cons
 // result. Same arithmetic, same order of summation as the main kernel.
 constexpr int LAT_NMAX = 8;
 
-template <bool NOLSE>
+// TT tokens per workgroup (16 or 8): with fewer tokens per workgroup a
+// small batch spreads over more CUs. Wave w owns token slots w and w + 8;
+// slots at or past TT are empty (zero codes, nothing loaded, nothing stored),
+// so MFMA columns of those slots carry zeros.
+template <bool NOLSE, int TT>
 __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
@@ -630,7 +634,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x % NH;
   const int tile = blockIdx.x / NH;
-  const int t0 = tile * TILE_T;
+  const int t0 = tile * TT;
   const int tl = lane & 15;
   const int kb = lane >> 4;
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
@@ -641,14 +645,14 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
   // the gate piece this thread writes at the end (token i / 16, 8 columns)
   const int tok = threadIdx.x >> 4, col = (threadIdx.x & 15) * 8;
   const int t_out = t0 + tok;
-  const bool out_live = threadIdx.x < STORE_LANES && t_out < a.S;
+  const bool out_live = tok < TT && t_out < a.S;
   const int64_t out_off = ((int64_t)t_out * GROWS + h * VD + col) * 2;
   uint4 g8 = make_uint4(0u, 0u, 0u, 0u);
   if (out_live) g8 = load_nt16(a.gate + out_off);
 
-  const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
+  const int ttA = wave, ttB = wave + WAVES;
   const int tA = t0 + ttA, tB = t0 + ttB;
-  const bool liveA = tA < a.S, liveB = tB < a.S;
+  const bool liveA = ttA < TT && tA < a.S, liveB = ttB < TT && tB < a.S;
   const bool useA = liveA && tA < batch_end, useB = liveB && tB < batch_end;
   uint32_t latA[4] = {0u, 0u, 0u, 0u}, latB[4] = {0u, 0u, 0u, 0u};
   if constexpr (NOLSE) {
@@ -851,14 +855,33 @@ int launched(hipError_t e) {
   return MLA_POST_OK;
 }
 
+// Tokens per workgroup of the one-tile instance: 16 when that gives every
+// CU a workgroup, else 8. Measured on the split-merge (S = 128) and gathered
+// 8-rank (S = 256) batches: 8 tokens 19% and 5% faster than 16, 4 tokens
+// slower than 8.
+int latency_tile(int S) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  return NH * ((S + TILE_T - 1) / TILE_T) >= cus ? TILE_T : TILE_T / 2;
+}
+
+template <bool NOLSE>
+int launch_latency(const KArgs& k, int S, hipStream_t stream) {
+  const int tt = latency_tile(S);
+  const dim3 grid((unsigned)(NH * ((S + tt - 1) / tt)));
+  if (tt == TILE_T) hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T>), grid, dim3(THREADS), 0, stream, k);
+  else hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T / 2>), grid, dim3(THREADS), 0, stream, k);
+  return launched(hipGetLastError());
+}
+
 template <bool NOLSE, int NCH>
 int launch(const KArgs& k, int S, hipStream_t stream) {
   const int ntiles = (S + TILE_T - 1) / TILE_T;
   const int wph = workgroups_per_head(S);
   if (wph == ntiles && NCH == 1 && (NOLSE || k.n <= LAT_NMAX)) {
     // latency regime: one tile per workgroup, everything issued up front
-    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE>), dim3((unsigned)(NH * ntiles)), dim3(THREADS), 0, stream, k);
-    return launched(hipGetLastError());
+    return launch_latency<NOLSE>(k, S, stream);
   }
   const unsigned grid = (unsigned)(NH * wph);
   hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k, wph);
