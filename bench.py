@@ -324,7 +324,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(
-            "bench.py measures one GPU only: the mla_post path has no multi-GPU stage in this build "
+            "bench.py measures one GPU only: the mla_post path has no multi-GPU stage "
             "(the decode-context-parallel exchange is not implemented); run with --gpus 1.",
             file=sys.stderr,
         )
