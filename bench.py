@@ -46,13 +46,23 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def live_rows(w) -> int:
+    """Partial rows that carry weight, counted from the workload's LSEs: a row
+    is live when its LSE is a finite number (NaN and +inf count as -inf);
+    every row is live when there are no LSEs."""
+    import numpy as np
+
+    if w.lse_buf is None:
+        return w.n * w.S * 12
+    v = w.notes["lse_logical"] if "lse_logical" in w.notes else w.lse_view()
+    return int(np.isfinite(v).sum())
+
+
 def algorithmic_bytes(w) -> dict:
     """Bytes the method must move per call: each partial row of non-zero
     weight (1 KiB, rows whose LSE is -inf, NaN or +inf are not read), every
     LSE (4 B), W_V once, the gate read and the core write (S x 1536 bf16 each)."""
-    import synth
-
-    live = synth.live_rows(w)
+    live = live_rows(w)
     n_lse = 0 if w.lse_buf is None else w.n * w.S * 12
     gate_core = 2 * w.S * 1536 * 2
     live_b = live * 1024 + n_lse * 4 + W_V_BYTES + gate_core

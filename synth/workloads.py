@@ -320,16 +320,3 @@ STANDARD = {
 }
 
 EXTRA = {"large_decode_request_major": large_decode_request_major}
-
-
-def live_rows(w: Workload) -> int:
-    """Partial rows that carry weight: those whose LSE is a finite number.
-
-    A row is live when its LSE is a finite number (NaN and +inf count as -inf).
-    Every row is live when there are no LSEs. Counting only; no arithmetic of
-    the method.
-    """
-    if w.lse_buf is None:
-        return w.n * w.S * NH
-    v = w.notes["lse_logical"] if "lse_logical" in w.notes else w.lse_view()
-    return int(np.isfinite(v).sum())

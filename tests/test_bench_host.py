@@ -37,7 +37,7 @@ def test_more_than_one_gpu_exits_with_message():
 def test_algorithmic_bytes_large_decode():
     w = synth.large_decode()
     alg = bench.algorithmic_bytes(w)
-    live = synth.live_rows(w)
+    live = bench.live_rows(w)
     assert alg["rows"] == 16 * 4096 * 12
     assert alg["live_rows"] == live < alg["rows"]
     w_v = 12 * 128 * 256 + 12 * 128 * 16
