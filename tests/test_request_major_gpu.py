@@ -171,3 +171,51 @@ def test_large_request_major_sampled(gpu_lib):
     st.update(C.check_t3(g["core"][tokens], g["codes"][tokens], g["scales"][tokens], d["w_codes"], d["w_scales"], w.gate[tokens]))
     st.update(C.check_t4(g["core"][tokens], ref, g["lat"][tokens], g["codes"][tokens], g["scales"][tokens]))
     say(f"{w.name}: sampled {len(tokens)} tokens {st}")
+
+
+@pytest.mark.parametrize(
+    "make",
+    [
+        # 16 splits: the persistent kernel even for one tile per workgroup
+        pytest.param(lambda: synth.request_major("rm_masked_n16", per=16, q=4, S=64, seed=46, compact=True,
+                                                 kv_zero=0.3, batch_rows=50), id="n16_S64"),
+        # several tiles per workgroup, the batch ending inside a tile
+        pytest.param(lambda: synth.request_major("rm_masked_long", per=16, q=4, S=1104, seed=47, compact=True,
+                                                 kv_zero=0.2, batch_rows=1001), id="n16_S1104"),
+    ],
+)
+def test_masks_persistent(gpu_lib, make):
+    """Push-side masks in the persistent kernel (the LSEs and KV lengths it
+    loads a tile ahead): masked partials count as -inf, tokens past the batch
+    are +0, every token checked against the oracle."""
+    w = make()
+    g, _, _ = check(gpu_lib, w)
+    end = int(w.qsl[w.S // w.q])
+    assert np.all(g["core"][end:] == 0) and np.all(g["lat"][end:] == 0)
+
+
+def test_no_lse_masks_persistent(gpu_lib):
+    """One partial without LSE at S = 1100 (the persistent kernel): a masked
+    request or a token past the batch gives +0, every other token keeps its
+    row bit for bit."""
+    m = gpu_lib
+    S, q = 1100, 4
+    R = S // q
+    w = synth.single_partial("nolse_masked_long", S, seed=48)
+    rng = np.random.default_rng(48)
+    kv = rng.integers(0, 4, size=R).astype(np.int32)  # a quarter of the requests have no KV
+    qsl = (np.arange(R + 1) * q).astype(np.int32)
+    qsl[R] = 1037
+    d = device_inputs(w)
+    say("no-LSE with masks, persistent")
+    core, lat, codes, scales = m.mla_post(
+        d["o"], None, d["w_v"], d["w_v_scale"], d["gate"], debug=True, q=q,
+        kv_lens=torch.from_numpy(kv).cuda(), qsl=torch.from_numpy(qsl).cuda(),
+    )
+    torch.cuda.synchronize()
+    lse = O.push_mask(np.zeros((1, S, 12), np.float32), q, kv[None, :], qsl)
+    ref = O.mla_post(w.o_view(), lse, d["w_codes"], d["w_scales"], w.gate)
+    lat = to_bits(lat)
+    C.check_t1(lat, ref, exact=True)
+    C.check_t4(to_bits(core), ref, strict=True)
+    assert np.all(lat[1037:] == 0)
