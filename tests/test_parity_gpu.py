@@ -143,6 +143,7 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         pytest.param(lambda: synth.dense_splits("S1", 5, 1, seed=15), id="S1"),
         pytest.param(lambda: synth.dense_splits("n1_with_lse", 1, 19, seed=13, p_neg_inf=0.3, p_nan=0.1, p_pos_inf=0.1), id="n1_lse"),
         pytest.param(lambda: synth.dense_splits("n65", 65, 9, seed=11, p_neg_inf=0.1), id="n65_two_chunks"),
+        pytest.param(lambda: synth.dense_splits("n200", 200, 5, seed=30, p_neg_inf=0.3), id="n200_four_chunks"),
         pytest.param(lambda: synth.dense_splits("n300", 300, 3, seed=12, p_neg_inf=0.5), id="n300_eight_chunks"),
         pytest.param(lambda: synth.dense_splits("nmax", 512, 2, seed=16, p_neg_inf=0.05), id="n_max_512"),
         pytest.param(lambda: synth.dense_splits("all_dead", 4, 20, seed=14, p_neg_inf=1.0), id="all_dead"),
@@ -179,12 +180,14 @@ def test_dead_rows_nan_inf_not_read(gpu_lib):
     assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
 
 
-def test_strided_weights_and_lse(gpu_lib):
+@pytest.mark.parametrize("n", [4, 16], ids=["one_tile_instance", "persistent"])
+def test_strided_weights_and_lse(gpu_lib, n):
     """W_V codes as a column slice of a wider buffer, scales stored with the
     block axis outermost, lse as a non-dense view: same result as the dense
-    layout, and equal to the oracle."""
+    layout, and equal to the oracle (4 splits: the one-tile instance; 16: the
+    persistent kernel)."""
     m = gpu_lib
-    w = synth.dense_splits("strided", 4, 33, seed=21, p_neg_inf=0.1)
+    w = synth.dense_splits("strided", n, 33, seed=21, p_neg_inf=0.1)
     d = device_inputs(w)
     base = run_debug(m, d)
     wide = torch.zeros((12, 128, 512), dtype=torch.uint8, device="cuda")
@@ -192,7 +195,7 @@ def test_strided_weights_and_lse(gpu_lib):
     w_v = wide[:, :, 128:384]
     sc_t = d["w_v_scale"].permute(2, 0, 1).contiguous()  # [16, 12, 128]
     w_s = sc_t.permute(1, 2, 0)  # logical [12, 128, 16], strides (128, 1, 1536)
-    lse_wide = torch.full((4, 33, 12, 3), float("nan"), device="cuda")
+    lse_wide = torch.full((n, 33, 12, 3), float("nan"), device="cuda")
     lse_wide[..., 1] = d["lse"]
     lse_v = lse_wide[..., 1]
     say("strided: w_v slice, scales block-major, lse stride 3")
