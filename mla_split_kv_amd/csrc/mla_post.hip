@@ -8,8 +8,10 @@
 //
 // Decomposition (this library's own, not the page's):
 //   workgroup = 8 waves of 64 lanes that own one head h for the whole launch
-//     and walk its 16-token tiles (k workgroups per head, k filling the
-//     device once); W_V[h]'s operands stay in registers throughout;
+//     and walk its 16-token tiles (k workgroups per head, WG_PER_CU per CU
+//     in the grid); W_V[h]'s operands stay in registers throughout; the 12
+//     heads of one token tile run as consecutive workgroups of one XCD, so
+//     they read each (token, split) 12 KiB block together behind one L2;
 //   merge: per tile, wave w owns tokens 2w and 2w+1; a token's partial row
 //     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced non-temporal
 //     16-byte load per lane, ROWS_IN_FLIGHT rows in flight, rows of weight 0
@@ -27,6 +29,9 @@
 //   epilogue: bf16(acc) x gate -> bf16 tiles are held in LDS and written
 //     when the workgroup's tiles are done: 16-byte non-temporal stores,
 //     tokens < S only.
+// Small batches (the grid fits the device at once, n <= 8) take a one-tile
+// instance that issues every load up front, with 8-token tiles when 16-token
+// tiles would leave CUs idle.
 
 #include <hip/hip_runtime.h>
 
@@ -52,9 +57,6 @@ constexpr int ROWS_IN_FLIGHT = 8;              // partial rows a wave loads befo
 constexpr int PF_ROWS = ROWS_IN_FLIGHT;        // first rows of the next tile issued before the barrier
 constexpr bool NT_ROWS = true;                 // partial rows loaded non-temporally
 constexpr int WG_PER_CU = 3;                   // workgroups per CU in the grid (2 resident at a time)
-#ifndef MLA_KERNEL_ATTRS
-#define MLA_KERNEL_ATTRS
-#endif
 constexpr int NBLK = KVL / 32;                 // 16 MXFP4 blocks per latent row
 constexpr int CODE_ROW = TILE_T * 16 + 16;     // LDS bytes per block row (+16 B skew)
 constexpr int LDS_CODES = NBLK * CODE_ROW;     // 4352 B per buffer
@@ -494,7 +496,7 @@ __device__ __forceinline__ void head_and_slot(int& h, int& slot) {
 }
 
 template <bool NOLSE, int NCH>
-__global__ __launch_bounds__(THREADS) MLA_KERNEL_ATTRS void mla_post_kernel(const KArgs a, int wg_per_head) {
+__global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg_per_head) {
   // two LDS buffers: a wave may merge tile i+1 while others still read tile i
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][LDS_SCALES];
