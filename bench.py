@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 KERNEL_SRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc", "mla_post.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_post_large_decode.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_post_kernel.json")
 W_V_BYTES = 12 * 128 * 256 + 12 * 128 * 16  # MXFP4 codes + E8M0 scales, read once per launch
 
 
@@ -239,8 +239,8 @@ def traffic_entry(workload: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
-        t = json.load(f)
-    if t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_sha():
+        t = json.load(f).get(workload)
+    if not t or t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_sha():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -254,10 +254,12 @@ def counter_kib(csv_path: str, kernel_substr: str) -> list:
         return [float(r["Counter_Value"]) for r in csv.DictReader(f) if kernel_substr in r["Kernel_Name"]]
 
 
-def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str) -> dict:
-    """HBM bytes per launch of the fused kernel from FETCH_SIZE / WRITE_SIZE
-    runs, each scaled by what the same counter reads for the plain 1 GiB copy
-    (true bytes / counter bytes). Writes TRAFFIC_FILE."""
+def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                 workload: str = "large_decode") -> dict:
+    """HBM bytes per launch of the fused kernel on `workload` from FETCH_SIZE /
+    WRITE_SIZE runs, each scaled by what the same counter reads for the plain
+    1 GiB copy (true bytes / counter bytes). Stored under the workload's name
+    in TRAFFIC_FILE (one entry per workload)."""
     import statistics
 
     copy_bytes = 1 << 30
@@ -270,8 +272,8 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
     fetch = fk * 1024 * f_scale
     write = wk * 1024 * w_scale
     out = {
-        "kernel": "mla_post_kernel<false, 1> (large decode workload)",
-        "workload": "large_decode",
+        "kernel": f"mla_post_kernel<false, 1> ({workload} workload)",
+        "workload": workload,
         "kernel_source_sha256": kernel_sha(),
         "fetch_kib_per_dispatch": fk,
         "write_kib_per_dispatch": wk,
@@ -283,8 +285,13 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
         "hbm_write_bytes": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
     }
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    table[workload] = out
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
+        json.dump(table, f, indent=1, sort_keys=True)
         f.write("\n")
     return out
 
@@ -359,7 +366,7 @@ def main() -> int:
     )
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(traffic_from(*args.traffic_from), indent=1))
+        print(json.dumps(traffic_from(*args.traffic_from, workload=args.workload), indent=1))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -74,15 +74,21 @@ def test_traffic_from_counters(tmp_path, monkeypatch):
     assert out["hbm_fetch_bytes"] == 102 * 1024 * 2  # median of the kernel's dispatches only
     assert out["hbm_write_bytes"] == 12 * 1024
     assert out["hbm_bytes_per_launch"] == 102 * 2048 + 12 * 1024
-    saved = json.load(open(tmp_path / "traffic.json"))
+    saved = json.load(open(tmp_path / "traffic.json"))["large_decode"]
     assert saved["workload"] == "large_decode" and saved["kernel_source_sha256"] == bench.kernel_sha()
     assert bench.traffic_entry("large_decode") == out["hbm_bytes_per_launch"]
     assert bench.traffic_entry("large_decode_request_major") is None  # taken on another workload
+    # a second workload's entry is added beside the first
+    rm = bench.traffic_from(*(str(tmp_path / n) for n in ("f.csv", "w.csv", "cf.csv", "cw.csv")),
+                            workload="large_decode_request_major")
+    assert bench.traffic_entry("large_decode_request_major") == rm["hbm_bytes_per_launch"]
+    assert bench.traffic_entry("large_decode") == out["hbm_bytes_per_launch"]
 
 
 def test_traffic_is_null_once_the_kernel_changes(tmp_path, monkeypatch):
     t = tmp_path / "traffic.json"
-    t.write_text(json.dumps({"workload": "large_decode", "kernel_source_sha256": "0" * 64, "hbm_bytes_per_launch": 1}))
+    t.write_text(json.dumps({"large_decode": {"workload": "large_decode", "kernel_source_sha256": "0" * 64,
+                                              "hbm_bytes_per_launch": 1}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(t))
     assert bench.traffic_entry("large_decode") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
