@@ -45,10 +45,11 @@ extern "C" {
 #define MLA_POST_VD 128     /* W_V rows (value width) per head */
 #define MLA_POST_GROWS 1536 /* gate / core row length = 12 * 128 */
 #define MLA_POST_NMAX 512   /* largest number of partials per (token, head) */
+#define MLA_POST_SMAX (1 << 30) /* largest number of tokens per call */
 
 /* Status codes (0 = success, negative = error). */
 #define MLA_POST_OK 0
-#define MLA_POST_EINVAL (-1)       /* null pointer, bad size, lse NULL with n > 1 */
+#define MLA_POST_EINVAL (-1)       /* null pointer, bad size (S above MLA_POST_SMAX among them), lse NULL with n > 1 */
 #define MLA_POST_ESTRIDE (-2)      /* a stride that is negative or not a multiple the loads need */
 #define MLA_POST_EALIGN (-3)       /* a pointer not aligned as its loads or stores need */
 #define MLA_POST_ERANGE (-4)       /* an offset that overflows 64-bit arithmetic */
@@ -70,7 +71,7 @@ extern "C" {
 typedef struct mla_post_args {
   uint32_t struct_size; /* sizeof(mla_post_args), or MLA_POST_ARGS_V1_SIZE */
   int32_t n;            /* partials per (token, head): splits or ranks, 1..MLA_POST_NMAX */
-  int32_t S;            /* tokens; 0 is a no-op */
+  int32_t S;            /* tokens, 0..MLA_POST_SMAX; 0 is a no-op */
   int32_t reserved;
 
   const void* o;            /* bf16 partials, device, 16-byte aligned */
@@ -135,7 +136,8 @@ int mla_post_check(const mla_post_args* a);
  * x + r*x_stride (elements, 16-byte aligned rows), its codes (cols/2 bytes) to
  * codes + r*c_stride and its E8M0 scale codes (cols/32 bytes) to
  * scales + r*s_stride (bytes). This is how W_V is put into MXFP4 from bf16.
- * Asynchronous on `stream`; same status codes.
+ * Asynchronous on `stream`; same status codes (rows above 2^34 give
+ * MLA_POST_ERANGE).
  */
 int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stride, uint8_t* codes,
                        int64_t c_stride, uint8_t* scales, int64_t s_stride, void* stream);

@@ -799,7 +799,7 @@ int check_args(const mla_post_args* in) {
   const int st = normalize(in, &na);
   if (st != MLA_POST_OK) return st;
   const mla_post_args* a = &na;
-  if (a->n < 1 || a->S < 0 || a->q < 0) return MLA_POST_EINVAL;
+  if (a->n < 1 || a->S < 0 || a->S > MLA_POST_SMAX || a->q < 0) return MLA_POST_EINVAL;
   if (a->n > MLA_POST_NMAX) return MLA_POST_EUNSUPPORTED;
   if (a->S == 0) return MLA_POST_OK;
   if (!a->o || !a->w_v || !a->w_v_scale || !a->gate || !a->core) return MLA_POST_EINVAL;
@@ -950,6 +950,7 @@ int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stri
   if (rows == 0 || cols == 0) return MLA_POST_OK;
   if (!x || !codes || !scales) return MLA_POST_EINVAL;
   if ((cols % 32) || cols > 8192) return MLA_POST_EUNSUPPORTED;
+  if (rows > (int64_t(1) << 34)) return MLA_POST_ERANGE;
   if (x_stride < 0 || c_stride < 0 || s_stride < 0 || (x_stride % 8) || (c_stride % 4)) return MLA_POST_ESTRIDE;
   if (!aligned(x, 16) || !aligned(codes, 4)) return MLA_POST_EALIGN;
   int64_t xsb;

@@ -201,6 +201,19 @@ def test_quantizer_validation(lib):
     assert q(0x1000, 0, 512, 512, 0x2000, 256, 0x3000, 16, None) == OK  # nothing to do
     assert q(0x1000, 1 << 60, 512, 512, 0x2000, 256, 0x3000, 16, None) == ERANGE
     assert q(0x1000, 4, 512, 1 << 62, 0x2000, 256, 0x3000, 16, None) == ERANGE
+    assert q(0x1000, (1 << 34) + 1, 512, 0, 0x2000, 0, 0x3000, 0, None) == ERANGE  # rows beyond the limit
+    assert q(0x1000, (1 << 63) - 1, 512, 0, 0x2000, 0, 0x3000, 0, None) == ERANGE  # no overflow in the grid
+
+
+def test_token_count_limit(lib):
+    """S up to MLA_POST_SMAX = 2^30 is accepted, above it is rejected (the
+    tile and token arithmetic stays far from overflow)."""
+    a = good_args(n=2, S=1 << 30)
+    assert check(lib, a) == OK
+    a = good_args(n=2, S=(1 << 30) + 4)
+    assert check(lib, a) == EINVAL
+    src = open(HEADER).read()
+    assert "#define MLA_POST_SMAX (1 << 30)" in src
 
 
 # ---------------------------------------------------------------- the Python binding's checks
