@@ -610,7 +610,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
 // ---------------------------------------------------------------- the latency-regime kernel
 
 // When the whole grid is resident at once (one token tile per workgroup) and
-// n <= LAT_NMAX, bandwidth is not the bound; the chain of dependent memory
+// n <= lat_nmax(TT), bandwidth is not the bound; the chain of dependent memory
 // round trips is (LSEs -> weights -> rows of one token -> rows of the other
 // -> gate). This kernel issues everything at once: W_V, the gate, the LSEs
 // and every partial row of both tokens, speculatively, before the weights
@@ -619,11 +619,16 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
 // result. Same arithmetic, same order of summation as the main kernel.
 constexpr int LAT_NMAX = 8;
 
+// Rows per token the one-tile instance can hold in registers at once: with
+// 8-token tiles a wave owns one token, so it can hold twice as many.
+constexpr int lat_nmax(int tt) { return tt <= WAVES ? 2 * LAT_NMAX : LAT_NMAX; }
+
 // TT tokens per workgroup (16 or 8): with fewer tokens per workgroup a
 // small batch spreads over more CUs. Wave w owns token slots w and w + 8;
 // slots at or past TT are empty (zero codes, nothing loaded, nothing stored),
 // so MFMA columns of those slots carry zeros.
-template <bool NOLSE, int TT>
+// NM: rows per token held at once (the instance for n <= NM).
+template <bool NOLSE, int TT, int NM>
 __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
@@ -672,14 +677,20 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
     int kA[1] = {1}, kB[1] = {1};
     if (useA) issue_lse<1>(a, tA, h, lane, lA, kA);
     if (useB) issue_lse<1>(a, tB, h, lane, lB, kB);
-    uint4 rA[LAT_NMAX], rB[LAT_NMAX];
+    // a second token per wave only when the tile has 16 tokens
+    static_assert(NM <= lat_nmax(TT), "rows held at once");
+    constexpr int NB = TT > WAVES ? NM : 1;
+    uint4 rA[NM], rB[NB];
     const uint8_t* baseA = row_base(a, tA, h);
     const uint8_t* baseB = row_base(a, tB, h);
 #pragma unroll
-    for (int j = 0; j < LAT_NMAX; ++j) {
-      rA[j] = rB[j] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < NM; ++j) {
+      rA[j] = make_uint4(0u, 0u, 0u, 0u);
       if (useA && j < a.n) rA[j] = load_row16(baseA + (int64_t)j * a.o_sj, lane);
-      if (useB && j < a.n) rB[j] = load_row16(baseB + (int64_t)j * a.o_sj, lane);
+      if constexpr (TT > WAVES) {
+        rB[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (useB && j < a.n) rB[j] = load_row16(baseB + (int64_t)j * a.o_sj, lane);
+      }
     }
     if (useA) {
       finish_lse<1>(a, lane, lA, kA);
@@ -692,11 +703,13 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
     float accA[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float accB[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < LAT_NMAX; ++j) {
+    for (int j = 0; j < NM; ++j) {
       const int wa = useA && j < a.n ? __builtin_amdgcn_readlane(__float_as_int(lA[0]), j) : 0;
-      const int wb = useB && j < a.n ? __builtin_amdgcn_readlane(__float_as_int(lB[0]), j) : 0;
       if (wa & 0x7FFFFFFF) fma_row(__int_as_float(wa), rA[j], accA);
-      if (wb & 0x7FFFFFFF) fma_row(__int_as_float(wb), rB[j], accB);
+      if constexpr (TT > WAVES) {
+        const int wb = useB && j < a.n ? __builtin_amdgcn_readlane(__float_as_int(lB[0]), j) : 0;
+        if (wb & 0x7FFFFFFF) fma_row(__int_as_float(wb), rB[j], accB);
+      }
     }
     if (useA) {
 #pragma unroll
@@ -869,11 +882,14 @@ int latency_tile(int S) {
 }
 
 template <bool NOLSE>
-int launch_latency(const KArgs& k, int S, hipStream_t stream) {
-  const int tt = latency_tile(S);
+int launch_latency(const KArgs& k, int S, int tt, hipStream_t stream) {
   const dim3 grid((unsigned)(NH * ((S + tt - 1) / tt)));
-  if (tt == TILE_T) hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T>), grid, dim3(THREADS), 0, stream, k);
-  else hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T / 2>), grid, dim3(THREADS), 0, stream, k);
+  if (tt == TILE_T)
+    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T, LAT_NMAX>), grid, dim3(THREADS), 0, stream, k);
+  else if (NOLSE || k.n <= LAT_NMAX)
+    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T / 2, LAT_NMAX>), grid, dim3(THREADS), 0, stream, k);
+  else if constexpr (!NOLSE)
+    hipLaunchKernelGGL((mla_post_latency_kernel<false, TILE_T / 2, 2 * LAT_NMAX>), grid, dim3(THREADS), 0, stream, k);
   return launched(hipGetLastError());
 }
 
@@ -881,9 +897,10 @@ template <bool NOLSE, int NCH>
 int launch(const KArgs& k, int S, hipStream_t stream) {
   const int ntiles = (S + TILE_T - 1) / TILE_T;
   const int wph = workgroups_per_head(S);
-  if (wph == ntiles && NCH == 1 && (NOLSE || k.n <= LAT_NMAX)) {
+  if (wph == ntiles && NCH == 1) {
     // latency regime: one tile per workgroup, everything issued up front
-    return launch_latency<NOLSE>(k, S, stream);
+    const int tt = latency_tile(S);
+    if (NOLSE || k.n <= lat_nmax(tt)) return launch_latency<NOLSE>(k, S, tt, stream);
   }
   const unsigned grid = (unsigned)(NH * wph);
   hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k, wph);

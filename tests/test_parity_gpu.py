@@ -142,6 +142,8 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         pytest.param(lambda: synth.dense_splits("ragged_S37", 3, 37, seed=10, p_neg_inf=0.2), id="ragged_S37"),
         pytest.param(lambda: synth.dense_splits("S1", 5, 1, seed=15), id="S1"),
         pytest.param(lambda: synth.dense_splits("n1_with_lse", 1, 19, seed=13, p_neg_inf=0.3, p_nan=0.1, p_pos_inf=0.1), id="n1_lse"),
+        # 16 splits on 8-token tiles: the one-tile instance holding 16 rows per token
+        pytest.param(lambda: synth.dense_splits("n16_small", 16, 50, seed=31, p_neg_inf=0.2), id="n16_one_tile"),
         pytest.param(lambda: synth.dense_splits("n65", 65, 9, seed=11, p_neg_inf=0.1), id="n65_two_chunks"),
         pytest.param(lambda: synth.dense_splits("n200", 200, 5, seed=30, p_neg_inf=0.3), id="n200_four_chunks"),
         pytest.param(lambda: synth.dense_splits("n300", 300, 3, seed=12, p_neg_inf=0.5), id="n300_eight_chunks"),
@@ -180,11 +182,11 @@ def test_dead_rows_nan_inf_not_read(gpu_lib):
     assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
 
 
-@pytest.mark.parametrize("n", [4, 16], ids=["one_tile_instance", "persistent"])
+@pytest.mark.parametrize("n", [4, 20], ids=["one_tile_instance", "persistent"])
 def test_strided_weights_and_lse(gpu_lib, n):
     """W_V codes as a column slice of a wider buffer, scales stored with the
     block axis outermost, lse as a non-dense view: same result as the dense
-    layout, and equal to the oracle (4 splits: the one-tile instance; 16: the
+    layout, and equal to the oracle (4 splits: the one-tile instance; 20: the
     persistent kernel)."""
     m = gpu_lib
     w = synth.dense_splits("strided", n, 33, seed=21, p_neg_inf=0.1)

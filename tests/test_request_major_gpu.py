@@ -176,18 +176,22 @@ def test_large_request_major_sampled(gpu_lib):
 @pytest.mark.parametrize(
     "make",
     [
-        # 16 splits: the persistent kernel even for one tile per workgroup
+        # 16 splits on 8-token tiles (the one-tile instance holding 16 rows)
         pytest.param(lambda: synth.request_major("rm_masked_n16", per=16, q=4, S=64, seed=46, compact=True,
                                                  kv_zero=0.3, batch_rows=50), id="n16_S64"),
+        # 20 splits: the persistent kernel with one tile per workgroup
+        pytest.param(lambda: synth.request_major("rm_masked_n20", per=20, q=4, S=64, seed=49, compact=True,
+                                                 kv_zero=0.3, batch_rows=50), id="n20_S64"),
         # several tiles per workgroup, the batch ending inside a tile
         pytest.param(lambda: synth.request_major("rm_masked_long", per=16, q=4, S=1104, seed=47, compact=True,
                                                  kv_zero=0.2, batch_rows=1001), id="n16_S1104"),
     ],
 )
 def test_masks_persistent(gpu_lib, make):
-    """Push-side masks in the persistent kernel (the LSEs and KV lengths it
-    loads a tile ahead): masked partials count as -inf, tokens past the batch
-    are +0, every token checked against the oracle."""
+    """Push-side masks with many splits (the persistent kernel, whose LSEs and
+    KV lengths are loaded a tile ahead, and the 16-row one-tile instance):
+    masked partials count as -inf, tokens past the batch are +0, every token
+    checked against the oracle."""
     w = make()
     g, _, _ = check(gpu_lib, w)
     end = int(w.qsl[w.S // w.q])
