@@ -870,15 +870,17 @@ int launched(hipError_t e) {
   return MLA_POST_OK;
 }
 
-// Tokens per workgroup of the one-tile instance: 16 when that gives every
-// CU a workgroup, else 8. Measured on the split-merge (S = 128) and gathered
-// 8-rank (S = 256) batches: 8 tokens 19% and 5% faster than 16, 4 tokens
-// slower than 8.
+// Tokens per workgroup of the one-tile instance: 8 while that grid stays
+// within 3 workgroups per CU, else 16 (with n > 8 the call then goes to the
+// persistent kernel). Measured at 256 CUs with n = 4, 8 and 16: 8-token tiles
+// are 8-19% faster up to S = 512 and 2-9% slower at S = 640 (1.25 waves of
+// workgroups); 4-token tiles are slower than 8.
 int latency_tile(int S) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  return NH * ((S + TILE_T - 1) / TILE_T) >= cus ? TILE_T : TILE_T / 2;
+  const int64_t wg8 = (int64_t)NH * ((S + TILE_T / 2 - 1) / (TILE_T / 2));
+  return wg8 <= 3 * (int64_t)cus ? TILE_T / 2 : TILE_T;
 }
 
 template <bool NOLSE>

@@ -152,10 +152,14 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         pytest.param(lambda: synth.dense_splits("wide_lse", 12, 24, seed=17, lse_normal=(0.0, 80.0)), id="wide_lse_spread"),
         pytest.param(lambda: synth.dcp_gathered("dcp3_pad", 3, 29, seed=18, head_stride_rows=40, dead_from=20), id="dcp3_padded"),
         pytest.param(lambda: synth.single_partial("no_merge_S5", 5, seed=19, o_sigma=300.0), id="no_merge_ragged"),
-        # the one-tile instance with 16-token tiles (S from 337 to 1024, n <= 8;
-        # smaller batches use 8-token tiles), ragged
-        pytest.param(lambda: synth.dense_splits("latency16", 4, 500, seed=28, p_neg_inf=0.1), id="latency16_S500"),
+        # the one-tile instance at 256 CUs: 8-token tiles up to S = 512 (with
+        # 9-16 splits in the 16-row form), 16-token tiles beyond (n <= 8; with
+        # more splits that range takes the persistent kernel)
+        pytest.param(lambda: synth.dense_splits("latency8_n8", 8, 500, seed=32, p_neg_inf=0.1), id="latency8_n8_S500"),
+        pytest.param(lambda: synth.dense_splits("latency8_n16", 16, 510, seed=33, p_neg_inf=0.2), id="latency8_n16_S510"),
+        pytest.param(lambda: synth.dense_splits("latency16", 4, 900, seed=28, p_neg_inf=0.1), id="latency16_S900"),
         pytest.param(lambda: synth.single_partial("latency16_no_lse", 700, seed=29), id="latency16_no_lse"),
+        pytest.param(lambda: synth.dense_splits("n16_S800", 16, 800, seed=34, p_neg_inf=0.2), id="n16_persistent_one_tile_each"),
         # S past one device-filling wave of workgroups (more than 64 tiles per
         # head at 256 CUs): the persistent kernel, with a ragged last tile
         pytest.param(lambda: synth.dense_splits("persistent_ragged", 3, 1030, seed=23, p_neg_inf=0.2), id="persistent_ragged"),
