@@ -67,6 +67,11 @@ extern "C" {
  *     with rank r's partial of local head h at gathered head r*12 + h:
  *     (o_sj, o_st, o_sh) = (12*512, head_rows*512, 512);
  *   - one partial, no LSE (n == 1, lse == NULL): o [S, 12, 512].
+ * A row whose merge weight is 0 (LSE -inf, NaN or +inf, or masked below)
+ * never contributes, whatever it holds (NaN and inf included). The kernels
+ * skip loading most such rows but not all (the small-batch kernel loads a
+ * token's rows together with its LSEs), so every row j < n of every token
+ * t < S must lie in readable device memory.
  */
 typedef struct mla_post_args {
   uint32_t struct_size; /* sizeof(mla_post_args), or MLA_POST_ARGS_V1_SIZE */
@@ -109,8 +114,8 @@ typedef struct mla_post_args {
    *   LSE (j, t, h) = lse + j*l_sj + r*l_sr + t*l_st + h*l_sh.
    * The page's dense layout of per = P / R slices per request in one tensor
    * [P, S, 12, 512] is (o_sj, o_sr, o_st) = (S*6144, per*S*6144, 6144) with
-   * n = per. Partial j of token t is empty (LSE taken as -inf, row not read)
-   * when kv_lens[j*kl_sj + r] == 0, or for every j when t >= qsl[R]. */
+   * n = per. Partial j of token t is empty (LSE taken as -inf, its row never
+   * used) when kv_lens[j*kl_sj + r] == 0, or for every j when t >= qsl[R]. */
   int32_t q;              /* tokens per request; 0 or 1 = one token each. S % q == 0 */
   int32_t reserved2;
   int64_t o_sr, l_sr;     /* elements per request index, >= 0; o_sr a multiple of 8 */

@@ -15,7 +15,8 @@
 //   merge: per tile, wave w owns tokens 2w and 2w+1; a token's partial row
 //     is 1 KiB = 64 lanes x 16 B, so each row is one coalesced non-temporal
 //     16-byte load per lane, ROWS_IN_FLIGHT rows in flight, rows of weight 0
-//     not loaded; software-pipelined over tiles: before the barrier of a
+//     not loaded (but for the first rows of a workgroup's first tile, issued
+//     with its LSEs); software-pipelined over tiles: before the barrier of a
 //     tile a wave computes the next tile's weights (LSEs loaded a tile
 //     earlier, DPP reductions) and issues that tile's first rows, so it
 //     keeps loads in flight through the barrier and the MFMAs;
@@ -302,13 +303,17 @@ __device__ __forceinline__ void issue_rows(const KArgs& a, const uint8_t* rowbas
 }
 
 // acc += the weighted rows of one (t, h), in the order j = 0, 1, .., n - 1;
-// with PRE the first PF_ROWS rows of chunk 0 are already in flight (pv, pw).
+// with PRE the first PF_ROWS rows of chunk 0 are already in flight (pv, pw),
+// and those of weight 0 are skipped (a workgroup's first tile loads them
+// before it knows the weights). Skipping a row of weight 0 gives the same
+// bits as adding its 0 * 0: the sum starts at +0 and never becomes -0.
 template <int NCH, bool PRE>
 __device__ __forceinline__ void merge_token(const KArgs& a, const uint8_t* rowbase, int lane, const float wts[NCH],
                                             const uint4 pv[PF_ROWS], const float pw[PF_ROWS], float acc[8]) {
   if constexpr (PRE) {
 #pragma unroll
-    for (int b = 0; b < PF_ROWS; ++b) fma_row(pw[b], pv[b], acc);
+    for (int b = 0; b < PF_ROWS; ++b)
+      if (__float_as_int(pw[b]) & 0x7FFFFFFF) fma_row(pw[b], pv[b], acc);
   }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -440,13 +445,48 @@ __device__ __forceinline__ void tile_weights(const KArgs& a, int tile, int batch
 }
 
 // The first PF_ROWS rows of this wave's first token of tile `tile` (weights
-// wA), issued early; a token that does not exist has weights 0, so nothing
-// is read for it.
+// wA), issued before the barrier of the tile ahead of it; a row of weight 0,
+// or of a token that does not exist, reads nothing.
 template <int NCH>
 __device__ __forceinline__ void issue_first_rows(const KArgs& a, int tile, int h, int wave, int lane,
                                                  const float wA[NCH], uint4 pv[PF_ROWS], float pw[PF_ROWS]) {
   const int tA = min(tile * TILE_T + wave * TOK_PER_WAVE, a.S - 1);
   issue_rows<PF_ROWS>(a, row_base(a, tA, h), lane, __float_as_int(wA[0]), 0, 0, pv, pw);
+}
+
+// The first tile of a workgroup: rows 0 .. PF_ROWS - 1 of the wave's first
+// token, issued together with its LSE loads, before the weights are known,
+// so that the first tile does not wait one more memory round trip. Only a
+// token past S or past the batch, or a row past n, reads nothing (a buffer
+// resource of zero bytes); rows of weight 0 are loaded but never used (the
+// merge skips them by a uniform branch, so NaN or inf stored there cannot
+// reach the sum).
+__device__ __forceinline__ void issue_first_rows_early(const KArgs& a, int tile, int batch_end, int h, int wave,
+                                                       int lane, uint4 pv[PF_ROWS]) {
+  const int t = tile * TILE_T + wave * TOK_PER_WAVE;
+  const bool use = t < a.S && t < batch_end;
+  const uint8_t* rowbase = row_base(a, min(t, a.S - 1), h);
+  const int nc = min(64, a.n);
+#pragma unroll
+  for (int b = 0; b < PF_ROWS; ++b) {
+    const uint8_t* p = rowbase + (int64_t)min(b, nc - 1) * a.o_sj;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p), (short)0, (use && b < nc) ? KVL * 2 : 0, BUF_WORD3);
+    const v4u v = (v4u)__builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, NT_ROWS ? 2 : 0);  // 2: nt
+    pv[b] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+}
+
+// The weights of those rows once known (wA0: chunk 0's weights, lane j
+// holding partial j's): 0 past n.
+__device__ __forceinline__ void first_row_weights(const KArgs& a, float wA0, float pw[PF_ROWS]) {
+  const int nc = min(64, a.n);
+#pragma unroll
+  for (int b = 0; b < PF_ROWS; ++b) {
+    int wb = __builtin_amdgcn_readlane(__float_as_int(wA0), b);
+    if (b >= nc) wb = 0;
+    pw[b] = __int_as_float(wb);
+  }
 }
 
 // 8 bf16 W_UV results times 8 bf16 gate values, each rounded once to bf16
@@ -514,10 +554,9 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   const int kb = lane >> 4;  // MFMA K block of this lane
 
   // W_V[h]'s operands for this wave's 16 rows stay in registers for every
-  // tile of the head.
+  // tile of the head (loaded below, after the first tile's loads).
   uint4 wv[4];
   int sa = 0;
-  load_wv(a, h, wave, tl, kb, wv, sa);
   // tokens at or past qsl[R] lie past the batch: every partial is empty
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
 
@@ -530,12 +569,19 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   float wA[NCH], wB[NCH];  // weights of the current tile
   uint4 pv[PF_ROWS];       // its first rows, in flight
   float pw[PF_ROWS];
+  // The first tile's LSEs and first rows go out together; W_V goes out after
+  // them, so that waiting for the LSEs does not wait for W_V (loads complete
+  // in issue order), which only the first MFMAs need. Measured on the large
+  // decode batch: 122.9 -> 121.5 us for W_V last, 120.7 us with the rows
+  // issued early.
   if constexpr (!NOLSE) {
     prefetch_lse<NCH>(a, slot, h, wave, lane, lA, kA, lB, kB);
+    issue_first_rows_early(a, slot, batch_end, h, wave, lane, pv);
     tile_weights<NCH>(a, slot, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
+    first_row_weights(a, wA[0], pw);
     prefetch_lse<NCH>(a, slot + wg_per_head, h, wave, lane, lA, kA, lB, kB);
-    issue_first_rows<NCH>(a, slot, h, wave, lane, wA, pv, pw);
   }
+  load_wv(a, h, wave, tl, kb, wv, sa);
 
 #pragma unroll 1
   for (int tile = slot, it = 0; tile < ntiles; tile += wg_per_head, ++it) {

@@ -173,10 +173,18 @@ def test_edge(gpu_lib, w):
         assert np.all(g["core"] == 0) and np.all(g["lat"] == 0) and np.all(g["scales"] == 1)
 
 
-def test_dead_rows_nan_inf_not_read(gpu_lib):
+@pytest.mark.parametrize(
+    "n,S",
+    [(6, 40), (16, 1100), (20, 70), (66, 20)],
+    ids=["one_tile_instance", "persistent_n16", "persistent_n20", "persistent_two_chunks"],
+)
+def test_dead_rows_nan_inf_unused(gpu_lib, n, S):
     """Rows of weight 0 hold NaN and inf: the result equals the oracle's, which
-    never touches them, and is finite."""
-    w = synth.dense_splits("poisoned_dead", 6, 40, seed=20, p_neg_inf=0.2, p_nan=0.1, p_pos_inf=0.1)
+    never touches them, and is finite. Both kernels load some such rows before
+    their weights are known (the one-tile instance all of its rows, the
+    persistent kernel the first 8 rows of each workgroup's first tile) and
+    must leave them out of the sum."""
+    w = synth.dense_splits(f"poisoned_dead_n{n}", n, S, seed=20, p_neg_inf=0.2, p_nan=0.1, p_pos_inf=0.1)
     lse = w.lse_view()
     dead = ~np.isfinite(lse)
     ob = w.o_buf.copy()
