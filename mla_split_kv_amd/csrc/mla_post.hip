@@ -30,9 +30,10 @@
 //   epilogue: bf16(acc) x gate -> bf16 tiles are held in LDS and written
 //     when the workgroup's tiles are done: 16-byte non-temporal stores,
 //     tokens < S only.
-// Small batches (the grid fits the device at once, n <= 8) take a one-tile
-// instance that issues every load up front, with 8-token tiles when 16-token
-// tiles would leave CUs idle.
+// Small batches (one token tile per workgroup fills the device at most once;
+// n <= 16 with 8-token tiles, n <= 8 with 16-token tiles) take a one-tile
+// instance that issues every load up front, with 8-token tiles while that
+// grid is at most 3 workgroups per CU.
 
 #include <hip/hip_runtime.h>
 
@@ -40,6 +41,7 @@
 
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "mla_post.h"
@@ -897,14 +899,29 @@ int check_args(const mla_post_args* in) {
   return MLA_POST_OK;
 }
 
+// Compute units of the current device (256 on an MI355X), asked of the
+// runtime once per device; 256 if the runtime cannot tell.
+int device_cus() {
+  constexpr int MAX_DEVICES = 64;
+  static std::atomic<int> cached[MAX_DEVICES];  // 0: not asked yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool slot = dev >= 0 && dev < MAX_DEVICES;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (slot) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 // Workgroups per head: enough to fill the device once (WG_PER_CU resident
 // workgroups on each CU), or one per token tile when there are fewer tiles.
 int workgroups_per_head(int S) {
   const int ntiles = (S + TILE_T - 1) / TILE_T;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
-  const int fill = (cus * WG_PER_CU) / NH;
+  const int fill = (device_cus() * WG_PER_CU) / NH;
   return ntiles < fill ? ntiles : (fill > 0 ? fill : 1);
 }
 
@@ -922,11 +939,8 @@ int launched(hipError_t e) {
 // are 8-19% faster up to S = 512 and 2-9% slower at S = 640 (1.25 waves of
 // workgroups); 4-token tiles are slower than 8.
 int latency_tile(int S) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
   const int64_t wg8 = (int64_t)NH * ((S + TILE_T / 2 - 1) / (TILE_T / 2));
-  return wg8 <= 3 * (int64_t)cus ? TILE_T / 2 : TILE_T;
+  return wg8 <= 3 * (int64_t)device_cus() ? TILE_T / 2 : TILE_T;
 }
 
 template <bool NOLSE>
@@ -952,12 +966,7 @@ int launch(const KArgs& k, int S, hipStream_t stream) {
   }
   const unsigned grid = (unsigned)(NH * wph);
   hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k, wph);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    g_hip_error = hipGetErrorString(e);
-    return MLA_POST_ELAUNCH;
-  }
-  return MLA_POST_OK;
+  return launched(hipGetLastError());
 }
 
 }  // namespace
@@ -1027,12 +1036,7 @@ int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stri
   if (blocks > 0x7FFFFFFF) return MLA_POST_ERANGE;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint8_t*>(x), rows, cols, x_stride * 2, codes, c_stride, scales, s_stride);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    g_hip_error = hipGetErrorString(e);
-    return MLA_POST_ELAUNCH;
-  }
-  return MLA_POST_OK;
+  return launched(hipGetLastError());
 }
 
 const char* mla_post_strerror(int status) {
