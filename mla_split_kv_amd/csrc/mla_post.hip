@@ -68,6 +68,7 @@ constexpr int OUT_ROW = VD * 2 + 16;           // LDS bytes per token of the out
 constexpr int LDS_OUT = TILE_T * OUT_ROW;      // 4352 B
 constexpr int STORE_LANES = TILE_T * VD * 2 / 16;  // 256 16-byte pieces per output tile
 constexpr int OUT_TILES = 8;                   // output tiles held in LDS before they are written
+constexpr int SPREAD_MIN_N = 6;                // n from which leftover tokens are dealt out evenly
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -405,39 +406,40 @@ __device__ __forceinline__ void merge_stage(const KArgs& a, int t, int tt, int h
   quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
 }
 
-// Raw LSEs of this wave's two tokens of token tile `tile` (issue_lse). The
-// loads are issued for every tile and token, the token index clamped to
-// S - 1, so that their number never varies; tokens past S or past the batch
-// and tiles that do not exist never use them.
+// Raw LSEs of this wave's two tokens of the tile starting at token t0
+// (issue_lse). The loads are issued for every tile and token, the token
+// index clamped to S - 1, so that their number never varies; tokens the
+// tile does not own, tokens past the batch and tiles that do not exist never
+// use them.
 template <int NCH>
-__device__ __forceinline__ void prefetch_lse(const KArgs& a, int tile, int h, int wave, int lane, float lA[NCH],
+__device__ __forceinline__ void prefetch_lse(const KArgs& a, int t0, int h, int wave, int lane, float lA[NCH],
                                              int kA[NCH], float lB[NCH], int kB[NCH]) {
-  const int tA = tile * TILE_T + wave * TOK_PER_WAVE;
+  const int tA = t0 + wave * TOK_PER_WAVE;
   issue_lse<NCH>(a, min(tA, a.S - 1), h, lane, lA, kA);
   issue_lse<NCH>(a, min(tA + 1, a.S - 1), h, lane, lB, kB);
 }
 
-// Merge weights of this wave's two tokens of token tile `tile` from their
-// raw LSEs (loaded a tile earlier); all zero for tokens past S or past the
-// batch, and for tiles that do not exist.
+// Merge weights of this wave's two tokens of the tile [t0, tend) from their
+// raw LSEs (loaded a tile earlier); all zero for tokens at or past tend or
+// past the batch, and for tiles that do not exist (tend <= t0).
 template <int NCH>
-__device__ __forceinline__ void tile_weights(const KArgs& a, int tile, int batch_end, int wave, int lane,
+__device__ __forceinline__ void tile_weights(const KArgs& a, int t0, int tend, int batch_end, int wave, int lane,
                                              const float lA[NCH], const int kA[NCH], const float lB[NCH],
                                              const int kB[NCH], float wA[NCH], float wB[NCH]) {
-  const int tA = tile * TILE_T + wave * TOK_PER_WAVE, tB = tA + 1;
+  const int tA = t0 + wave * TOK_PER_WAVE, tB = tA + 1;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     wA[c] = lA[c];
     wB[c] = lB[c];
   }
-  if (tA < a.S && tA < batch_end) {
+  if (tA < tend && tA < batch_end) {
     finish_lse<NCH>(a, lane, wA, kA);
     lse_to_weights<NCH>(wA);
   } else {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) wA[c] = 0.f;
   }
-  if (tB < a.S && tB < batch_end) {
+  if (tB < tend && tB < batch_end) {
     finish_lse<NCH>(a, lane, wB, kB);
     lse_to_weights<NCH>(wB);
   } else {
@@ -446,27 +448,27 @@ __device__ __forceinline__ void tile_weights(const KArgs& a, int tile, int batch
   }
 }
 
-// The first PF_ROWS rows of this wave's first token of tile `tile` (weights
-// wA), issued before the barrier of the tile ahead of it; a row of weight 0,
-// or of a token that does not exist, reads nothing.
+// The first PF_ROWS rows of this wave's first token of the tile starting at
+// token t0 (weights wA), issued before the barrier of the tile ahead of it;
+// a row of weight 0, or of a token the tile does not own, reads nothing.
 template <int NCH>
-__device__ __forceinline__ void issue_first_rows(const KArgs& a, int tile, int h, int wave, int lane,
+__device__ __forceinline__ void issue_first_rows(const KArgs& a, int t0, int h, int wave, int lane,
                                                  const float wA[NCH], uint4 pv[PF_ROWS], float pw[PF_ROWS]) {
-  const int tA = min(tile * TILE_T + wave * TOK_PER_WAVE, a.S - 1);
+  const int tA = min(t0 + wave * TOK_PER_WAVE, a.S - 1);
   issue_rows<PF_ROWS>(a, row_base(a, tA, h), lane, __float_as_int(wA[0]), 0, 0, pv, pw);
 }
 
 // The first tile of a workgroup: rows 0 .. PF_ROWS - 1 of the wave's first
 // token, issued together with its LSE loads, before the weights are known,
 // so that the first tile does not wait one more memory round trip. Only a
-// token past S or past the batch, or a row past n, reads nothing (a buffer
-// resource of zero bytes); rows of weight 0 are loaded but never used (the
-// merge skips them by a uniform branch, so NaN or inf stored there cannot
-// reach the sum).
-__device__ __forceinline__ void issue_first_rows_early(const KArgs& a, int tile, int batch_end, int h, int wave,
-                                                       int lane, uint4 pv[PF_ROWS]) {
-  const int t = tile * TILE_T + wave * TOK_PER_WAVE;
-  const bool use = t < a.S && t < batch_end;
+// token the tile [t0, tend) does not own or past the batch, or a row past n,
+// reads nothing (a buffer resource of zero bytes); rows of weight 0 are
+// loaded but never used (the merge skips them by a uniform branch, so NaN or
+// inf stored there cannot reach the sum).
+__device__ __forceinline__ void issue_first_rows_early(const KArgs& a, int t0, int tend, int batch_end, int h,
+                                                       int wave, int lane, uint4 pv[PF_ROWS]) {
+  const int t = t0 + wave * TOK_PER_WAVE;
+  const bool use = t < tend && t < batch_end;
   const uint8_t* rowbase = row_base(a, min(t, a.S - 1), h);
   const int nc = min(64, a.n);
 #pragma unroll
@@ -500,16 +502,67 @@ __device__ __forceinline__ uint4 gate_mul(const uint4& av, const uint4& g8) {
                     pack_bf16(bf_lo(av.w) * bf_lo(g8.w), bf_hi(av.w) * bf_hi(g8.w)));
 }
 
-// Write `count` staged output tiles (final core values) of head h, tiles
-// first, first + step, ..: each token's 256 bytes of the head go out as 16
+// The token tiles of one slot of a head, out of k slots per head. Every slot
+// takes `main` full 16-token tiles at stride k (tiles slot, slot + k, ..);
+// the tokens past those, fewer than 16 k, go out as one more tile of at
+// most `chunk` consecutive tokens per slot. With `spread` they are dealt out
+// evenly (chunk = ceil(rest / k) <= 16), so every workgroup's share of a head
+// differs from another's by at most one short tile and the CUs, each running
+// the same number of workgroups, end together; otherwise whole 16-token tiles
+// go to the first slots. Measured with 16 splits: S = 2064 72.9 -> 63.4 us,
+// 4112 124.3 -> 121.3 us, 4608 139.7 -> 135.1 us spread; with 6 to 12 splits
+// spreading is as good or better at most sizes, with 2 or 4 splits (little
+// data per tile, so an extra short tile costs a whole memory round trip)
+// it loses as often as it wins, so those keep whole tiles. The schedule's
+// arithmetic costs about 0.3% where nothing is left over (S = 4096: 120.8
+// -> 121.2 us in an A/B run).
+struct TileSched {
+  int S, k, slot;
+  int main;   // full tiles of every slot
+  int base;   // the first token past them
+  int chunk;  // tokens of a slot's short tile
+  int count;  // tiles of this slot
+};
+
+__device__ __forceinline__ TileSched tile_sched(int S, int k, int slot, bool spread) {
+  TileSched t;
+  t.S = S;
+  t.k = k;
+  t.slot = slot;
+  t.main = S / (TILE_T * k);
+  t.base = t.main * TILE_T * k;
+  const int rest = S - t.base;
+  t.chunk = spread ? (rest + k - 1) / k : min(rest, TILE_T);
+  t.count = t.main + (t.base + slot * t.chunk < S ? 1 : 0);
+  return t;
+}
+
+// Tokens [t0, tend) of tile i of the slot; t0 = tend = S for an i past its
+// tiles.
+__device__ __forceinline__ void tile_span(const TileSched& t, int i, int& t0, int& tend) {
+  if (i < t.main) {
+    t0 = (t.slot + i * t.k) * TILE_T;
+    tend = t0 + TILE_T;
+  } else if (i < t.count) {
+    t0 = t.base + t.slot * t.chunk;
+    tend = min(t0 + t.chunk, t.S);
+  } else {
+    t0 = tend = t.S;
+  }
+}
+
+// Write `count` staged output tiles (final core values) of head h, the slot's
+// tiles first, first + 1, ..: each token's 256 bytes of the head go out as 16
 // coalesced 16-byte pieces; the whole workgroup shares the pieces.
-__device__ __forceinline__ void flush_tiles(const KArgs& a, int h, int first, int step, int count,
+__device__ __forceinline__ void flush_tiles(const KArgs& a, const TileSched& ts, int h, int first, int count,
                                             uint8_t (*s_out)[LDS_OUT]) {
   for (int i = threadIdx.x; i < count * STORE_LANES; i += THREADS) {
     const int k = i / STORE_LANES, piece = i % STORE_LANES;
     const int tok = piece >> 4, col = (piece & 15) * 8;
-    const int t = (first + k * step) * TILE_T + tok;
-    if (t >= a.S) continue;
+    int t0, tend;
+    tile_span(ts, first + k, t0, tend);
+    const int t = t0 + tok;
+    if (t >= tend) continue;
     const int64_t off = ((int64_t)t * GROWS + h * VD + col) * 2;
     store_nt16(a.core + off, *reinterpret_cast<const uint4*>(s_out[k] + tok * OUT_ROW + col * 2));
   }
@@ -549,9 +602,9 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   // stays in scalar registers, and row loads take a scalar base plus the
   // lane's 32-bit offset
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int h, slot;  // this workgroup's head, fixed, and its token tiles slot, slot + wg_per_head, ...
+  int h, slot;  // this workgroup's head, fixed, and its slot of the head's tiles
   head_and_slot(h, slot);
-  const int ntiles = (a.S + TILE_T - 1) / TILE_T;
+  const TileSched ts = tile_sched(a.S, wg_per_head, slot, NOLSE || a.n >= SPREAD_MIN_N);
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
@@ -576,28 +629,33 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   // in issue order), which only the first MFMAs need. Measured on the large
   // decode batch: 122.9 -> 121.5 us for W_V last, 120.7 us with the rows
   // issued early.
+  // tokens of the current tile and of the next one
+  int t0, tend, n0, nend;
+  tile_span(ts, 0, t0, tend);
+  tile_span(ts, 1, n0, nend);
   if constexpr (!NOLSE) {
-    prefetch_lse<NCH>(a, slot, h, wave, lane, lA, kA, lB, kB);
-    issue_first_rows_early(a, slot, batch_end, h, wave, lane, pv);
-    tile_weights<NCH>(a, slot, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
+    prefetch_lse<NCH>(a, t0, h, wave, lane, lA, kA, lB, kB);
+    issue_first_rows_early(a, t0, tend, batch_end, h, wave, lane, pv);
+    tile_weights<NCH>(a, t0, tend, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
     first_row_weights(a, wA[0], pw);
-    prefetch_lse<NCH>(a, slot + wg_per_head, h, wave, lane, lA, kA, lB, kB);
+    prefetch_lse<NCH>(a, n0, h, wave, lane, lA, kA, lB, kB);
   }
   load_wv(a, h, wave, tl, kb, wv, sa);
 
 #pragma unroll 1
-  for (int tile = slot, it = 0; tile < ntiles; tile += wg_per_head, ++it) {
+  for (int it = 0; it < ts.count; ++it) {
     uint8_t* codes = s_codes[it & 1];
     uint8_t* scales = s_scales[it & 1];
-    const int t0 = tile * TILE_T;
+    int m0, mend;  // the tile after the next
+    tile_span(ts, it + 2, m0, mend);
     // ---- merge + quantise: wave owns tile slots 2 wave and 2 wave + 1
     const int ttA = wave * TOK_PER_WAVE, ttB = ttA + 1;
     const int tA = t0 + ttA, tB = t0 + ttB;
-    const bool liveA = tA < a.S, liveB = tB < a.S;
+    const bool liveA = tA < tend, liveB = tB < tend;
     const bool emptyA = tA >= batch_end, emptyB = tB >= batch_end;
     // the 4 gate values of this lane's outputs (token tl, rows v0..v0+3),
     // loaded now so that their latency hides behind the merge; a token past
-    // S re-reads row S - 1 (its output is never stored)
+    // S re-reads row S - 1 (a token the tile does not own is never stored)
     const int t_out = min(t0 + tl, a.S - 1);
     const uint2 g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
     if constexpr (NOLSE) {
@@ -608,10 +666,9 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
       merge_stage<NCH, false>(a, tB, ttB, h, lane, liveB, emptyB, wB, pv, pw, codes, scales);
     }
     if constexpr (!NOLSE) {
-      const int next = tile + wg_per_head;
-      tile_weights<NCH>(a, next, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
-      prefetch_lse<NCH>(a, next + wg_per_head, h, wave, lane, lA, kA, lB, kB);
-      issue_first_rows<NCH>(a, next, h, wave, lane, wA, pv, pw);
+      tile_weights<NCH>(a, n0, nend, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
+      prefetch_lse<NCH>(a, m0, h, wave, lane, lA, kA, lB, kB);
+      issue_first_rows<NCH>(a, n0, h, wave, lane, wA, pv, pw);
     }
     // One barrier per tile: it publishes this tile's codes, and since every
     // wave finished the previous tile's MFMAs before merging this one, the
@@ -646,12 +703,16 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
     *reinterpret_cast<uint2*>(s_out[slot_out] + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
         make_uint2(pack_bf16(bf_lo(ab.x) * bf_lo(g4.x), bf_hi(ab.x) * bf_hi(g4.x)),
                    pack_bf16(bf_lo(ab.y) * bf_lo(g4.y), bf_hi(ab.y) * bf_hi(g4.y)));
-    const bool last = tile + wg_per_head >= ntiles;
+    const bool last = it + 1 == ts.count;
     if (slot_out == OUT_TILES - 1 || last) {
       __syncthreads();
-      flush_tiles(a, h, tile - slot_out * wg_per_head, wg_per_head, slot_out + 1, s_out);
+      flush_tiles(a, ts, h, it - slot_out, slot_out + 1, s_out);
       if (!last) __syncthreads();  // the staging buffers are reused
     }
+    t0 = n0;
+    tend = nend;
+    n0 = m0;
+    nend = mend;
   }
 }
 
