@@ -124,10 +124,11 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
     edges = [0, 1, 15, 16, 17, 1007, 1023, 1024, 1025, w.S - 2, w.S - 1]
     if w.S > 8192:  # the first tile after a mid-kernel flush, and around it
         edges += [8 * 1024 - 1, 8 * 1024, 8 * 1024 + 15, 8 * 1024 + 16]
-    # the short tiles the tokens past the full ones are dealt out as (64 slots
-    # per head at 256 CUs): around the first three and the last
-    base = (w.S // 1024) * 1024
-    chunk = -(-(w.S - base) // 64)
+    # the short tiles the tokens past the full ones are dealt out as (at 256
+    # CUs: 64 slots per head, 40 from 65 to 96 tiles): around the first three
+    k = 40 if 64 < -(-w.S // 16) <= 96 else 64
+    base = (w.S // (16 * k)) * 16 * k
+    chunk = -(-(w.S - base) // k)
     if chunk:
         edges += [base + c * chunk + d for c in (0, 1, 2) for d in (-1, 0, 1)]
     edges = [t for t in edges if 0 <= t < w.S]
