@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MLA_POST_VERSION 2
+#define MLA_POST_VERSION 3
 
 /* Fixed shapes (the page's per-rank Kimi-K3 shapes at 8-way tensor parallelism). */
 #define MLA_POST_HEADS 12   /* local heads */
@@ -134,6 +134,32 @@ int mla_post(const mla_post_args* a, void* stream);
 /* The validation of mla_post alone: host only, touches no device memory and
  * needs no GPU. Returns what mla_post would return before launching. */
 int mla_post_check(const mla_post_args* a);
+
+/* Since version 3: the launch mla_post makes for a call. */
+#define MLA_POST_KERNEL_NONE 0       /* S == 0: nothing is launched */
+#define MLA_POST_KERNEL_ONE_TILE 1   /* one token tile per workgroup, every load issued up front */
+#define MLA_POST_KERNEL_PERSISTENT 2 /* workgroups that each keep one head and walk its tiles */
+
+typedef struct mla_post_plan {
+  int32_t kernel;              /* MLA_POST_KERNEL_* */
+  int32_t tile_tokens;         /* tokens of a full tile: 8 or 16 */
+  int32_t rows_held;           /* one-tile kernel: partial rows per token held at once (8 or 16); else 0 */
+  int32_t lse_chunks;          /* persistent kernel: 64-lane chunks of partials per token (1, 2, 4 or 8); else 1 */
+  int32_t workgroups_per_head; /* the grid is 12 times this */
+  int32_t workgroups;          /* grid size (workgroups of 512 threads) */
+  int32_t full_tiles;          /* persistent kernel: full 16-token tiles of every workgroup */
+  int32_t short_tokens;        /* persistent kernel: tokens of one more, shorter tile per workgroup (at most
+                                  16; the last workgroups of a head may get fewer or none); 0: none */
+  int32_t cus;                 /* compute units the plan was made for */
+} mla_post_plan;
+
+/* Since version 3: validate like mla_post_check and, on MLA_POST_OK, fill
+ * *out with the launch mla_post would make for these arguments on a device
+ * with `cus` compute units (cus <= 0: the current HIP device, asked of the
+ * runtime once; 256 when it cannot tell). Host only; touches no device
+ * memory and needs no GPU when cus > 0. Returns a status code; out == NULL
+ * is MLA_POST_EINVAL. */
+int mla_post_plan_for(const mla_post_args* a, int32_t cus, mla_post_plan* out);
 
 /*
  * Quantise `rows` rows of `cols` bf16 values (cols a multiple of 32, at most

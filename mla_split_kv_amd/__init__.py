@@ -75,9 +75,32 @@ class MlaPostArgs(ctypes.Structure):
 ARGS_V1_SIZE = 176  # MLA_POST_ARGS_V1_SIZE: the struct up to dbg_scales
 
 
+class MlaPostPlan(ctypes.Structure):
+    """mla_post_plan: the launch mla_post makes for a call."""
+
+    _fields_ = [
+        (name, ctypes.c_int32)
+        for name in (
+            "kernel",
+            "tile_tokens",
+            "rows_held",
+            "lse_chunks",
+            "workgroups_per_head",
+            "workgroups",
+            "full_tiles",
+            "short_tokens",
+            "cus",
+        )
+    ]
+
+
+KERNELS = {0: "none", 1: "one_tile", 2: "persistent"}  # MLA_POST_KERNEL_*
+
+
 EXPORTS = (
     "mla_post",
     "mla_post_check",
+    "mla_post_plan_for",
     "mla_quantize_mxfp4",
     "mla_post_strerror",
     "mla_post_last_hip_error",
@@ -105,6 +128,8 @@ def load() -> ctypes.CDLL:
     lib.mla_post.restype = ctypes.c_int
     lib.mla_post_check.argtypes = [ctypes.POINTER(MlaPostArgs)]
     lib.mla_post_check.restype = ctypes.c_int
+    lib.mla_post_plan_for.argtypes = [ctypes.POINTER(MlaPostArgs), ctypes.c_int32, ctypes.POINTER(MlaPostPlan)]
+    lib.mla_post_plan_for.restype = ctypes.c_int
     lib.mla_quantize_mxfp4.argtypes = [
         ctypes.c_void_p,
         ctypes.c_int64,
@@ -220,6 +245,23 @@ def make_args(o, lse, w_v, w_v_scale, gate, core, dbg=None, q=1, o_sr=0, l_sr=0,
         _need(scales.dtype == torch.uint8 and tuple(scales.shape) == (S, NH, KVL // 32) and scales.is_contiguous(), ValueError, "dbg scales")
         a.dbg_lat, a.dbg_codes, a.dbg_scales = lat.data_ptr(), codes.data_ptr(), scales.data_ptr()
     return a
+
+
+def plan_args(a: MlaPostArgs, cus: int = 0) -> dict:
+    """mla_post_plan_for on a filled struct: the launch mla_post would make on
+    a device with ``cus`` compute units (0: the current device). Host only."""
+    lib = load()
+    out = MlaPostPlan()
+    _raise(lib, lib.mla_post_plan_for(ctypes.byref(a), int(cus), ctypes.byref(out)))
+    d = {name: getattr(out, name) for name, _ in MlaPostPlan._fields_}
+    d["kernel"] = KERNELS[d["kernel"]]
+    return d
+
+
+def plan(o, lse, w_v, w_v_scale, gate, core=None, cus: int = 0, **layout) -> dict:
+    """The launch mla_post would make for these tensors (same arguments as
+    mla_post; nothing is launched and no device memory is touched)."""
+    return plan_args(make_args(o, lse, w_v, w_v_scale, gate, gate if core is None else core, **layout), cus)
 
 
 def mla_post(o, lse, w_v, w_v_scale, gate, core=None, debug: bool = False, **layout):

@@ -524,15 +524,23 @@ struct TileSched {
   int count;  // tiles of this slot
 };
 
+// Full tiles per slot and the short tile's token count (host and device).
+__host__ __device__ inline void tile_counts(int S, int k, bool spread, int& main, int& chunk) {
+  main = S / (TILE_T * k);
+  const int rest = S - main * TILE_T * k;
+  chunk = spread ? (rest + k - 1) / k : (rest < TILE_T ? rest : TILE_T);
+}
+
+// Whether leftover tokens are dealt out evenly (see TileSched).
+__host__ __device__ inline bool spread_leftover(bool nolse, int n) { return nolse || n >= SPREAD_MIN_N; }
+
 __device__ __forceinline__ TileSched tile_sched(int S, int k, int slot, bool spread) {
   TileSched t;
   t.S = S;
   t.k = k;
   t.slot = slot;
-  t.main = S / (TILE_T * k);
+  tile_counts(S, k, spread, t.main, t.chunk);
   t.base = t.main * TILE_T * k;
-  const int rest = S - t.base;
-  t.chunk = spread ? (rest + k - 1) / k : min(rest, TILE_T);
   t.count = t.main + (t.base + slot * t.chunk < S ? 1 : 0);
   return t;
 }
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int h, slot;  // this workgroup's head, fixed, and its slot of the head's tiles
   head_and_slot(h, slot);
-  const TileSched ts = tile_sched(a.S, wg_per_head, slot, NOLSE || a.n >= SPREAD_MIN_N);
+  const TileSched ts = tile_sched(a.S, wg_per_head, slot, spread_leftover(NOLSE, a.n));
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
@@ -988,9 +996,8 @@ int device_cus() {
 // 24 splits, 40 against 64: 16 splits S = 1100 43.5 -> 36.7 us, S = 1280
 // 45.4 -> 40.3 us, within 2% either way at S = 1536, and 64 ahead again from
 // about 100 tiles.
-int workgroups_per_head(int S) {
+int workgroups_per_head(int S, int cus) {
   const int ntiles = (S + TILE_T - 1) / TILE_T;
-  const int cus = device_cus();
   const int fill = max(1, cus * WG_PER_CU / NH);
   if (ntiles <= fill) return ntiles;
   const int one_round = (2 * cus / NH) / XCDS * XCDS;
@@ -1011,34 +1018,79 @@ int launched(hipError_t e) {
 // persistent kernel). Measured at 256 CUs with n = 4, 8 and 16: 8-token tiles
 // are 8-19% faster up to S = 512 and 2-9% slower at S = 640 (1.25 waves of
 // workgroups); 4-token tiles are slower than 8.
-int latency_tile(int S) {
+int latency_tile(int S, int cus) {
   const int64_t wg8 = (int64_t)NH * ((S + TILE_T / 2 - 1) / (TILE_T / 2));
-  return wg8 <= 3 * (int64_t)device_cus() ? TILE_T / 2 : TILE_T;
+  return wg8 <= 3 * (int64_t)cus ? TILE_T / 2 : TILE_T;
+}
+
+// 64-lane LSE chunks the persistent kernel is instantiated for.
+int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
+
+// The launch for a validated call with S > 0 on a device of `cus` CUs: the
+// one-tile instance when one token tile per workgroup fills the device at
+// most once and the instance can hold every row of a token, else the
+// persistent kernel. mla_post launches exactly this.
+mla_post_plan make_plan(const mla_post_args* a, int cus) {
+  mla_post_plan p;
+  memset(&p, 0, sizeof(p));
+  p.cus = cus;
+  const bool nolse = a->lse == nullptr;
+  const int S = a->S, n = a->n;
+  const int nch = nolse ? 1 : lse_chunks(n);
+  const int ntiles = (S + TILE_T - 1) / TILE_T;
+  const int wph = workgroups_per_head(S, cus);
+  if (wph == ntiles && nch == 1) {
+    const int tt = latency_tile(S, cus);
+    if (nolse || n <= lat_nmax(tt)) {
+      p.kernel = MLA_POST_KERNEL_ONE_TILE;
+      p.tile_tokens = tt;
+      p.rows_held = nolse ? 1 : (tt == TILE_T || n <= LAT_NMAX) ? LAT_NMAX : 2 * LAT_NMAX;
+      p.lse_chunks = 1;
+      p.workgroups_per_head = (S + tt - 1) / tt;
+      p.workgroups = NH * p.workgroups_per_head;
+      return p;
+    }
+  }
+  p.kernel = MLA_POST_KERNEL_PERSISTENT;
+  p.tile_tokens = TILE_T;
+  p.lse_chunks = nch;
+  p.workgroups_per_head = wph;
+  p.workgroups = NH * wph;
+  tile_counts(S, wph, spread_leftover(nolse, n), p.full_tiles, p.short_tokens);
+  return p;
 }
 
 template <bool NOLSE>
-int launch_latency(const KArgs& k, int S, int tt, hipStream_t stream) {
-  const dim3 grid((unsigned)(NH * ((S + tt - 1) / tt)));
-  if (tt == TILE_T)
-    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T, LAT_NMAX>), grid, dim3(THREADS), 0, stream, k);
-  else if (NOLSE || k.n <= LAT_NMAX)
-    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T / 2, LAT_NMAX>), grid, dim3(THREADS), 0, stream, k);
+void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.workgroups), block(THREADS);
+  if (p.tile_tokens == TILE_T)
+    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T, LAT_NMAX>), grid, block, 0, stream, k);
+  else if (p.rows_held <= LAT_NMAX)
+    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T / 2, LAT_NMAX>), grid, block, 0, stream, k);
   else if constexpr (!NOLSE)
-    hipLaunchKernelGGL((mla_post_latency_kernel<false, TILE_T / 2, 2 * LAT_NMAX>), grid, dim3(THREADS), 0, stream, k);
-  return launched(hipGetLastError());
+    hipLaunchKernelGGL((mla_post_latency_kernel<false, TILE_T / 2, 2 * LAT_NMAX>), grid, block, 0, stream, k);
 }
 
-template <bool NOLSE, int NCH>
-int launch(const KArgs& k, int S, hipStream_t stream) {
-  const int ntiles = (S + TILE_T - 1) / TILE_T;
-  const int wph = workgroups_per_head(S);
-  if (wph == ntiles && NCH == 1) {
-    // latency regime: one tile per workgroup, everything issued up front
-    const int tt = latency_tile(S);
-    if (NOLSE || k.n <= lat_nmax(tt)) return launch_latency<NOLSE>(k, S, tt, stream);
+int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t stream) {
+  if (p.kernel == MLA_POST_KERNEL_ONE_TILE) {
+    if (nolse)
+      launch_one_tile<true>(k, p, stream);
+    else
+      launch_one_tile<false>(k, p, stream);
+    return launched(hipGetLastError());
   }
-  const unsigned grid = (unsigned)(NH * wph);
-  hipLaunchKernelGGL((mla_post_kernel<NOLSE, NCH>), dim3(grid), dim3(THREADS), 0, stream, k, wph);
+  const dim3 grid((unsigned)p.workgroups), block(THREADS);
+  const int wph = p.workgroups_per_head;
+  if (nolse)
+    hipLaunchKernelGGL((mla_post_kernel<true, 1>), grid, block, 0, stream, k, wph);
+  else if (p.lse_chunks == 1)
+    hipLaunchKernelGGL((mla_post_kernel<false, 1>), grid, block, 0, stream, k, wph);
+  else if (p.lse_chunks == 2)
+    hipLaunchKernelGGL((mla_post_kernel<false, 2>), grid, block, 0, stream, k, wph);
+  else if (p.lse_chunks == 4)
+    hipLaunchKernelGGL((mla_post_kernel<false, 4>), grid, block, 0, stream, k, wph);
+  else
+    hipLaunchKernelGGL((mla_post_kernel<false, 8>), grid, block, 0, stream, k, wph);
   return launched(hipGetLastError());
 }
 
@@ -1083,12 +1135,23 @@ int mla_post(const mla_post_args* in, void* stream) {
   k.kv_lens = a->kv_lens;
   k.kl_sj = a->kl_sj;
   k.qsl = a->qsl;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!a->lse) return launch<true, 1>(k, a->S, s);
-  if (a->n <= 64) return launch<false, 1>(k, a->S, s);
-  if (a->n <= 128) return launch<false, 2>(k, a->S, s);
-  if (a->n <= 256) return launch<false, 4>(k, a->S, s);
-  return launch<false, 8>(k, a->S, s);
+  return launch_plan(k, make_plan(a, device_cus()), a->lse == nullptr, static_cast<hipStream_t>(stream));
+}
+
+int mla_post_plan_for(const mla_post_args* in, int32_t cus, mla_post_plan* out) {
+  if (!out) return MLA_POST_EINVAL;
+  const int st = check_args(in);
+  if (st != MLA_POST_OK) return st;
+  const int c = cus > 0 ? cus : device_cus();
+  if (in->S == 0) {
+    memset(out, 0, sizeof(*out));
+    out->cus = c;
+    return MLA_POST_OK;
+  }
+  mla_post_args na;
+  normalize(in, &na);
+  *out = make_plan(&na, c);
+  return MLA_POST_OK;
 }
 
 int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stride, uint8_t* codes, int64_t c_stride,

@@ -77,7 +77,7 @@ def test_struct_layout_matches_binding(probe_output):
 
 def test_versions_agree(probe_output):
     sizes, _, _ = probe_output
-    assert sizes["header_version"] == sizes["library_version"] == 2
+    assert sizes["header_version"] == sizes["library_version"] == 3
 
 
 def test_status_codes_from_c(probe_output):

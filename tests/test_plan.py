@@ -1,0 +1,155 @@
+"""The launch plan (mla_post_plan_for) on the CPU: which kernel, tiling and
+grid a call gets, as the host code routes it. mla_post launches exactly this
+plan, so these tests pin the routing the GPU tests rely on to reach every
+kernel instance, and check that the persistent kernel's schedule covers every
+token of every head exactly once."""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import mla_split_kv_amd as m
+
+
+def args(n, S, lse=True):
+    """Valid arguments with fake (never dereferenced) device addresses."""
+    a = m.MlaPostArgs()
+    a.struct_size = ctypes.sizeof(m.MlaPostArgs)
+    a.n, a.S = n, S
+    a.o = 0x100000
+    a.o_sj, a.o_st, a.o_sh = S * 6144, 6144, 512
+    if lse:
+        a.lse = 0x200000
+        a.l_sj, a.l_st, a.l_sh = S * 12, 12, 1
+    a.w_v = 0x300000
+    a.w_sh, a.w_sv = 128 * 256, 256
+    a.w_v_scale = 0x400000
+    a.s_sh, a.s_sv, a.s_sb = 128 * 16, 16, 1
+    a.gate = 0x500000
+    a.core = 0x600000
+    return a
+
+
+def plan(n, S, lse=True, cus=256):
+    return m.plan_args(args(n, S, lse), cus)
+
+
+# (n, S, lse) -> the expected plan at 256 CUs, from the documented rules:
+# one-tile instance while one tile per workgroup fits 64 workgroups per head
+# and the instance holds every row (8-token tiles up to 3 workgroups per CU,
+# i.e. S <= 512, with 16 rows; 16-token tiles with 8 rows); else the
+# persistent kernel with 64 workgroups per head, 40 from 65 to 96 tiles, and
+# leftover tokens dealt out evenly from n = 6 (whole 16-token tiles below).
+TABLE = [
+    # the five standard workloads
+    ((2, 4, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=1, workgroups=12)),
+    ((1, 64, False), dict(kernel="one_tile", tile_tokens=8, rows_held=1, workgroups_per_head=8, workgroups=96)),
+    ((8, 128, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=16, workgroups=192)),
+    ((8, 256, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=32, workgroups=384)),
+    ((16, 4096, True), dict(kernel="persistent", tile_tokens=16, lse_chunks=1, workgroups_per_head=64, workgroups=768,
+                            full_tiles=4, short_tokens=0)),
+    # one-tile boundaries
+    ((16, 512, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16, workgroups_per_head=64, workgroups=768)),
+    ((8, 513, True), dict(kernel="one_tile", tile_tokens=16, rows_held=8, workgroups_per_head=33)),
+    ((4, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=8, workgroups_per_head=64)),
+    ((1, 1000, False), dict(kernel="one_tile", tile_tokens=16, rows_held=1, workgroups_per_head=63)),
+    ((16, 513, True), dict(kernel="persistent", workgroups_per_head=33, full_tiles=0, short_tokens=16)),
+    ((17, 64, True), dict(kernel="persistent", workgroups_per_head=4, full_tiles=1, short_tokens=0)),
+    ((1, 1025, False), dict(kernel="persistent", workgroups_per_head=40)),
+    # the one-round rule (65 to 96 tiles) and the leftover deal
+    ((16, 1100, True), dict(kernel="persistent", workgroups_per_head=40, workgroups=480, full_tiles=1, short_tokens=12)),
+    ((4, 1100, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=1, short_tokens=16)),
+    ((16, 1536, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=2, short_tokens=7)),
+    ((16, 1552, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=1, short_tokens=9)),
+    ((16, 4112, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=4, short_tokens=1)),
+    ((5, 4112, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=4, short_tokens=16)),
+    ((16, 9000, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=8, short_tokens=13)),
+    # LSE chunks
+    ((64, 100, True), dict(kernel="persistent", lse_chunks=1)),
+    ((65, 100, True), dict(kernel="persistent", lse_chunks=2)),
+    ((200, 100, True), dict(kernel="persistent", lse_chunks=4)),
+    ((512, 2, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=1)),
+]
+
+
+@pytest.mark.parametrize("key,expect", TABLE, ids=[f"n{k[0]}_S{k[1]}{'' if k[2] else '_nolse'}" for k, _ in TABLE])
+def test_routing_table_at_256_cus(key, expect):
+    p = plan(*key)
+    assert p["cus"] == 256
+    for field, value in expect.items():
+        assert p[field] == value, (field, p)
+    if p["kernel"] == "one_tile":
+        assert p["lse_chunks"] == 1 and p["full_tiles"] == 0 and p["short_tokens"] == 0
+    else:
+        assert p["tile_tokens"] == 16 and p["rows_held"] == 0
+
+
+def test_empty_batch_launches_nothing():
+    p = plan(4, 0)
+    assert p["kernel"] == "none" and p["workgroups"] == 0 and p["cus"] == 256
+
+
+def test_invalid_arguments_give_the_check_status():
+    lib = m.load()
+    a = args(4, 8)
+    a.o = 0x100001  # misaligned
+    out = m.MlaPostPlan()
+    assert lib.mla_post_plan_for(ctypes.byref(a), 256, ctypes.byref(out)) == lib.mla_post_check(ctypes.byref(a)) == -3
+    assert lib.mla_post_plan_for(ctypes.byref(args(4, 8)), 256, None) == -1
+
+
+def covered(p, S):
+    """Token -> number of persistent workgroups of one head that own it, from
+    the plan's fields and the schedule rule (full tiles at stride k, then the
+    leftover tokens in consecutive runs of short_tokens, slot by slot)."""
+    k, main, chunk = p["workgroups_per_head"], p["full_tiles"], p["short_tokens"]
+    count = np.zeros(S, dtype=np.int64)
+    for slot in range(k):
+        for i in range(main):
+            t0 = (slot + i * k) * 16
+            count[t0 : t0 + 16] += 1
+        base = main * 16 * k
+        t0 = base + slot * chunk
+        if chunk and t0 < S:
+            count[t0 : min(t0 + chunk, S)] += 1
+    return count
+
+
+@pytest.mark.parametrize("cus", [256, 304, 80, 32])
+def test_schedule_covers_every_token_once(cus):
+    """Over many (n, S): each token of a head belongs to exactly one workgroup,
+    short tiles hold at most 16 tokens, and the grid is 12 per head; the
+    one-tile instance's grid covers S."""
+    rng = np.random.default_rng(cus)
+    sizes = sorted(set([1, 2, 15, 16, 17, 500, 1023, 1024, 1025, 1100, 1536, 1537, 2064, 4096, 4112, 9000]
+                       + list(rng.integers(1, 20000, size=60))))
+    for S in sizes:
+        for n, lse in ((1, False), (1, True), (4, True), (6, True), (16, True), (100, True)):
+            p = plan(n, int(S), lse, cus)
+            assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["cus"] == cus
+            if p["kernel"] == "one_tile":
+                assert p["workgroups_per_head"] * p["tile_tokens"] >= S > (p["workgroups_per_head"] - 1) * p["tile_tokens"]
+                continue
+            assert 0 <= p["short_tokens"] <= 16
+            c = covered(p, int(S))
+            assert np.all(c == 1), (n, S, cus, p)
+
+
+def test_current_device_without_gpu_assumes_256():
+    """cus = 0 asks the HIP runtime; with no GPU it cannot tell and the plan is
+    made for 256 CUs (an MI355X). On a GPU machine the device's own count."""
+    p = m.plan_args(args(16, 4096), 0)
+    assert p["cus"] > 0
+    if p["cus"] == 256:
+        assert p == plan(16, 4096)
+
+
+@pytest.mark.gpu
+def test_device_plan_is_the_table(gpu_lib):
+    """On the MI355X the current device has 256 CUs, so the plans mla_post
+    launches there are the ones the table above pins."""
+    for (n, S, lse), _ in TABLE:
+        assert m.plan_args(args(n, S, lse), 0) == plan(n, S, lse)
