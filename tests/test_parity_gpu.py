@@ -271,6 +271,36 @@ def test_deterministic(gpu_lib):
     assert np.array_equal(a, b)
 
 
+def test_concurrent_streams(gpu_lib):
+    """Calls running at the same time on two streams (default priority) do not
+    interfere: the library keeps no device state between or across calls. A
+    persistent-kernel call and a one-tile call, and two calls of the same
+    workload into different outputs, each equal their serial result."""
+    m = gpu_lib
+    wa = synth.dense_splits("conc_persistent", 16, 1100, seed=70, p_neg_inf=0.05)
+    wb = synth.dense_splits("conc_small", 8, 128, seed=71, p_neg_inf=0.1)
+    da, db = device_inputs(wa), device_inputs(wb)
+    say("concurrent streams")
+    ref_a = to_bits(m.mla_post(da["o"], da["lse"], da["w_v"], da["w_v_scale"], da["gate"]))
+    ref_b = to_bits(m.mla_post(db["o"], db["lse"], db["w_v"], db["w_v_scale"], db["gate"]))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a = [torch.full((wa.S, 1536), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    outs_b = [torch.full((wb.S, 1536), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    outs_a2 = [torch.full((wa.S, 1536), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    for i in range(4):
+        with torch.cuda.stream(s1):
+            m.mla_post(da["o"], da["lse"], da["w_v"], da["w_v_scale"], da["gate"], outs_a[i])
+        with torch.cuda.stream(s2):
+            m.mla_post(db["o"], db["lse"], db["w_v"], db["w_v_scale"], db["gate"], outs_b[i])
+            m.mla_post(da["o"], da["lse"], da["w_v"], da["w_v_scale"], da["gate"], outs_a2[i])
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert np.array_equal(to_bits(outs_a[i]), ref_a)
+        assert np.array_equal(to_bits(outs_a2[i]), ref_a)
+        assert np.array_equal(to_bits(outs_b[i]), ref_b)
+
+
 def test_ranks_helper_matches_view(gpu_lib):
     """mla_post_ranks on the gathered [S, 104, 512] buffer equals mla_post on
     the explicit [R, S, 12, 512] view."""
