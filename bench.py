@@ -60,7 +60,7 @@ def live_rows(w) -> int:
 
 def algorithmic_bytes(w) -> dict:
     """Bytes the method must move per call: each partial row of non-zero
-    weight (1 KiB, rows whose LSE is -inf, NaN or +inf are not read), every
+    weight (1 KiB; rows whose LSE is -inf, NaN or +inf need not be read), every
     LSE (4 B), W_V once, the gate read and the core write (S x 1536 bf16 each)."""
     live = live_rows(w)
     n_lse = 0 if w.lse_buf is None else w.n * w.S * 12
