@@ -296,19 +296,20 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
     return out
 
 
-def size_sweep(sizes: list, steps: int, warmup: int, m, torch) -> dict:
+def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16) -> dict:
     """Microseconds per call and the roofline fraction at several batch sizes
-    S, with the large decode batch's distributions (16 splits, o ~ N(0, 2),
-    lse ~ N(8, 6) with 5% -inf, seed 4), generated once at the largest size;
-    each size takes the first S tokens of it (strided views, as a caller
-    would pass them)."""
+    S, with the large decode batch's distributions (16 splits unless given,
+    o ~ N(0, 2), lse ~ N(8, 6) with 5% -inf, seed 4), generated once at the
+    largest size; each size takes the first S tokens of it (strided views, as
+    a caller would pass them)."""
     import numpy as np
 
     import synth
 
     smax = max(sizes)
-    log(f"generating 16 splits x {smax} tokens ({16 * smax * 12 * 1024 / 1e6:.0f} MB of partials)")
-    w = synth.dense_splits(f"large_decode_S{smax}", 16, smax, seed=4, o_sigma=2.0, lse_normal=(8.0, 6.0), p_neg_inf=0.05)
+    log(f"generating {splits} splits x {smax} tokens ({splits * smax * 12 * 1024 / 1e6:.0f} MB of partials)")
+    w = synth.dense_splits(f"sweep_n{splits}_S{smax}", splits, smax, seed=4, o_sigma=2.0, lse_normal=(8.0, 6.0),
+                           p_neg_inf=0.05)
     d = device_setup(w, m, torch)
     live_by_token = np.isfinite(w.lse_view()).sum(axis=(0, 2))
     rows = []
@@ -316,13 +317,13 @@ def size_sweep(sizes: list, steps: int, warmup: int, m, torch) -> dict:
         call = m.prepare(d["o"][:, :S], d["lse"][:, :S], d["w_v"], d["w_s"], d["gate"][:S], d["core"][:S])
         t = time_gpu(call, steps, warmup, torch)
         us = 1e3 * t["event_ms"] / steps
-        alg = int(live_by_token[:S].sum()) * 1024 + 16 * S * 12 * 4 + W_V_BYTES + 2 * S * 1536 * 2
+        alg = int(live_by_token[:S].sum()) * 1024 + splits * S * 12 * 4 + W_V_BYTES + 2 * S * 1536 * 2
         gbps = alg / (us * 1e-6) / 1e9
         rows.append({"S": S, "us_per_call": round(us, 3), "GBps": round(gbps, 1),
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "tokens_per_s": round(S / (us * 1e-6), 1),
-                     "alg_bytes": alg})
+                     "alg_bytes": alg, "plan": m.plan(d["o"][:, :S], d["lse"][:, :S], d["w_v"], d["w_s"], d["gate"][:S])})
         log(f"S={S}: {rows[-1]}")
-    return {"size_sweep": rows, "workload": "16 splits, large decode distributions, first S tokens", "steps": steps}
+    return {"size_sweep": rows, "workload": f"{splits} splits, large decode distributions, first S tokens", "steps": steps}
 
 
 def calibrate_copy(torch) -> None:
@@ -358,6 +359,7 @@ def main() -> int:
     ap.add_argument("--all", action="store_true", help="also time the four other standard workloads (stderr)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--sizes", help="comma-separated batch sizes S: print a size sweep (one JSON object) instead")
+    ap.add_argument("--splits", type=int, default=16, help="partials per (token, head) of the size sweep")
     ap.add_argument(
         "--traffic-from",
         nargs=4,
@@ -395,7 +397,8 @@ def main() -> int:
     if args.sizes:
         torch.cuda.set_device(0)
         m.load()
-        print(json.dumps(size_sweep([int(x) for x in args.sizes.split(",")], args.steps, args.warmup, m, torch)))
+        sizes = [int(x) for x in args.sizes.split(",")]
+        print(json.dumps(size_sweep(sizes, args.steps, args.warmup, m, torch, args.splits)))
         return 0
 
     log(f"generating the {args.workload} workload (seeded, 805 MB of partials)")

@@ -150,6 +150,8 @@ typedef struct mla_post_plan {
   int32_t full_tiles;          /* persistent kernel: full 16-token tiles of every workgroup */
   int32_t short_tokens;        /* persistent kernel: tokens of one more, shorter tile per workgroup (at most
                                   16; the last workgroups of a head may get fewer or none); 0: none */
+  int32_t pair_rows;           /* persistent kernel: rows of each of a wave's two tokens issued a tile ahead
+                                  (4, for n <= 4 with LSEs); 0: 8 rows of its first token only */
   int32_t cus;                 /* compute units the plan was made for */
 } mla_post_plan;
 

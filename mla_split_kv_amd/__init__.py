@@ -89,6 +89,7 @@ class MlaPostPlan(ctypes.Structure):
             "workgroups",
             "full_tiles",
             "short_tokens",
+            "pair_rows",
             "cus",
         )
     ]

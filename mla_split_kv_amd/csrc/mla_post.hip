@@ -306,23 +306,23 @@ __device__ __forceinline__ void issue_rows(const KArgs& a, const uint8_t* rowbas
 }
 
 // acc += the weighted rows of one (t, h), in the order j = 0, 1, .., n - 1;
-// with PRE the first PF_ROWS rows of chunk 0 are already in flight (pv, pw),
-// and those of weight 0 are skipped (a workgroup's first tile loads them
-// before it knows the weights). Skipping a row of weight 0 gives the same
-// bits as adding its 0 * 0: the sum starts at +0 and never becomes -0.
-template <int NCH, bool PRE>
+// the first NPRE rows of chunk 0 are already in flight (pv, pw), and those
+// of weight 0 are skipped (a workgroup's first tile loads them before it
+// knows the weights). Skipping a row of weight 0 gives the same bits as
+// adding its 0 * 0: the sum starts at +0 and never becomes -0. REST: rows
+// past the first NPRE may exist (false when the caller guarantees n <= NPRE).
+template <int NCH, int NPRE, bool REST>
 __device__ __forceinline__ void merge_token(const KArgs& a, const uint8_t* rowbase, int lane, const float wts[NCH],
-                                            const uint4 pv[PF_ROWS], const float pw[PF_ROWS], float acc[8]) {
-  if constexpr (PRE) {
+                                            const uint4* pv, const float* pw, float acc[8]) {
 #pragma unroll
-    for (int b = 0; b < PF_ROWS; ++b)
-      if (__float_as_int(pw[b]) & 0x7FFFFFFF) fma_row(pw[b], pv[b], acc);
-  }
+  for (int b = 0; b < NPRE; ++b)
+    if (__float_as_int(pw[b]) & 0x7FFFFFFF) fma_row(pw[b], pv[b], acc);
+  if constexpr (!REST) return;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int nc = min(64, a.n - 64 * c);
     const int wbits = __float_as_int(wts[c]);
-    for (int j0 = (PRE && c == 0) ? PF_ROWS : 0; j0 < nc; j0 += ROWS_IN_FLIGHT) {
+    for (int j0 = c == 0 ? NPRE : 0; j0 < nc; j0 += ROWS_IN_FLIGHT) {
       uint4 v[ROWS_IN_FLIGHT];
       float w[ROWS_IN_FLIGHT];
       issue_rows<ROWS_IN_FLIGHT>(a, rowbase, lane, wbits, c, j0, v, w);
@@ -377,29 +377,29 @@ __device__ __forceinline__ const uint8_t* row_base(const KArgs& a, int t, int h)
   return a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (int64_t)(t / a.q) * a.o_sr;
 }
 
-// One partial and no LSE: token t's row (tile slot tt) is the attention
-// output itself, used as the bf16 latents unless its request is masked as
-// having no KV or the token lies past the batch (`empty`); -> MXFP4 into LDS.
+// One partial and no LSE: token t's row (tile slot tt, already loaded: v)
+// is the attention output itself, used as the bf16 latents unless its
+// request is masked as having no KV or the token lies past the batch
+// (`empty`); -> MXFP4 into LDS.
 __device__ __forceinline__ void copy_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
-                                           uint8_t* s_codes, uint8_t* s_scales) {
+                                           const uint4& v, uint8_t* s_codes, uint8_t* s_scales) {
   uint32_t lat[4] = {0u, 0u, 0u, 0u};
   if (live && !empty && !(a.kv_lens && a.kv_lens[t / a.q] == 0)) {
-    const uint4 v = load_row16(row_base(a, t, h), lane);
     lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
   }
   quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
 }
 
 // Token t (tile slot tt) of the persistent kernel with LSEs: merged latents
-// -> bf16 -> MXFP4 into LDS. With PRE its first PF_ROWS rows are in flight.
-template <int NCH, bool PRE>
+// -> bf16 -> MXFP4 into LDS. Its first NPRE rows are in flight (pv, pw).
+template <int NCH, int NPRE, bool REST>
 __device__ __forceinline__ void merge_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
-                                            const float wts[NCH], const uint4 pv[PF_ROWS], const float pw[PF_ROWS],
+                                            const float wts[NCH], const uint4* pv, const float* pw,
                                             uint8_t* s_codes, uint8_t* s_scales) {
   uint32_t lat[4] = {0u, 0u, 0u, 0u};
   if (live && !empty) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    merge_token<NCH, PRE>(a, row_base(a, t, h), lane, wts, pv, pw, acc);
+    merge_token<NCH, NPRE, REST>(a, row_base(a, t, h), lane, wts, pv, pw, acc);
 #pragma unroll
     for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
   }
@@ -448,31 +448,40 @@ __device__ __forceinline__ void tile_weights(const KArgs& a, int t0, int tend, i
   }
 }
 
-// The first PF_ROWS rows of this wave's first token of the tile starting at
-// token t0 (weights wA), issued before the barrier of the tile ahead of it;
-// a row of weight 0, or of a token the tile does not own, reads nothing.
-template <int NCH>
-__device__ __forceinline__ void issue_first_rows(const KArgs& a, int t0, int h, int wave, int lane,
-                                                 const float wA[NCH], uint4 pv[PF_ROWS], float pw[PF_ROWS]) {
+// Rows of this wave's tokens of the tile starting at token t0 that are
+// issued before the barrier of the tile ahead of it (weights wA, wB): with
+// PAIR = 0 the first PF_ROWS rows of the first token; with PAIR > 0 the
+// first PAIR rows of each of the two tokens (slots 0..PAIR-1 and
+// PAIR..2 PAIR-1), which for n <= PAIR is every row of the tile. A row of
+// weight 0, or of a token the tile does not own, reads nothing.
+template <int NCH, int PAIR>
+__device__ __forceinline__ void issue_next_rows(const KArgs& a, int t0, int h, int wave, int lane, const float wA[NCH],
+                                                const float wB[NCH], uint4* pv, float* pw) {
   const int tA = min(t0 + wave * TOK_PER_WAVE, a.S - 1);
-  issue_rows<PF_ROWS>(a, row_base(a, tA, h), lane, __float_as_int(wA[0]), 0, 0, pv, pw);
+  if constexpr (PAIR == 0) {
+    issue_rows<PF_ROWS>(a, row_base(a, tA, h), lane, __float_as_int(wA[0]), 0, 0, pv, pw);
+  } else {
+    const int tB = min(t0 + wave * TOK_PER_WAVE + 1, a.S - 1);
+    issue_rows<PAIR>(a, row_base(a, tA, h), lane, __float_as_int(wA[0]), 0, 0, pv, pw);
+    issue_rows<PAIR>(a, row_base(a, tB, h), lane, __float_as_int(wB[0]), 0, 0, pv + PAIR, pw + PAIR);
+  }
 }
 
-// The first tile of a workgroup: rows 0 .. PF_ROWS - 1 of the wave's first
-// token, issued together with its LSE loads, before the weights are known,
-// so that the first tile does not wait one more memory round trip. Only a
-// token the tile [t0, tend) does not own or past the batch, or a row past n,
-// reads nothing (a buffer resource of zero bytes); rows of weight 0 are
-// loaded but never used (the merge skips them by a uniform branch, so NaN or
-// inf stored there cannot reach the sum).
-__device__ __forceinline__ void issue_first_rows_early(const KArgs& a, int t0, int tend, int batch_end, int h,
-                                                       int wave, int lane, uint4 pv[PF_ROWS]) {
-  const int t = t0 + wave * TOK_PER_WAVE;
+// The first tile of a workgroup: the rows issue_next_rows would issue for
+// it, issued together with its LSE loads, before the weights are known, so
+// that the first tile does not wait one more memory round trip. Only a token
+// the tile [t0, tend) does not own or past the batch, or a row past n, reads
+// nothing (a buffer resource of zero bytes); rows of weight 0 are loaded but
+// never used (the merge skips them by a uniform branch, so NaN or inf stored
+// there cannot reach the sum).
+template <int R>
+__device__ __forceinline__ void issue_rows_early(const KArgs& a, int t, int tend, int batch_end, int h, int lane,
+                                                 uint4* pv) {
   const bool use = t < tend && t < batch_end;
   const uint8_t* rowbase = row_base(a, min(t, a.S - 1), h);
   const int nc = min(64, a.n);
 #pragma unroll
-  for (int b = 0; b < PF_ROWS; ++b) {
+  for (int b = 0; b < R; ++b) {
     const uint8_t* p = rowbase + (int64_t)min(b, nc - 1) * a.o_sj;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(p), (short)0, (use && b < nc) ? KVL * 2 : 0, BUF_WORD3);
@@ -481,15 +490,38 @@ __device__ __forceinline__ void issue_first_rows_early(const KArgs& a, int t0, i
   }
 }
 
-// The weights of those rows once known (wA0: chunk 0's weights, lane j
+template <int PAIR>
+__device__ __forceinline__ void issue_first_rows_early(const KArgs& a, int t0, int tend, int batch_end, int h,
+                                                       int wave, int lane, uint4* pv) {
+  const int t = t0 + wave * TOK_PER_WAVE;
+  if constexpr (PAIR == 0) {
+    issue_rows_early<PF_ROWS>(a, t, tend, batch_end, h, lane, pv);
+  } else {
+    issue_rows_early<PAIR>(a, t, tend, batch_end, h, lane, pv);
+    issue_rows_early<PAIR>(a, t + 1, tend, batch_end, h, lane, pv + PAIR);
+  }
+}
+
+// The weights of R early rows once known (w0: chunk 0's weights, lane j
 // holding partial j's): 0 past n.
-__device__ __forceinline__ void first_row_weights(const KArgs& a, float wA0, float pw[PF_ROWS]) {
+template <int R>
+__device__ __forceinline__ void early_row_weights(const KArgs& a, float w0, float* pw) {
   const int nc = min(64, a.n);
 #pragma unroll
-  for (int b = 0; b < PF_ROWS; ++b) {
-    int wb = __builtin_amdgcn_readlane(__float_as_int(wA0), b);
+  for (int b = 0; b < R; ++b) {
+    int wb = __builtin_amdgcn_readlane(__float_as_int(w0), b);
     if (b >= nc) wb = 0;
     pw[b] = __int_as_float(wb);
+  }
+}
+
+template <int PAIR>
+__device__ __forceinline__ void first_row_weights(const KArgs& a, float wA0, float wB0, float* pw) {
+  if constexpr (PAIR == 0) {
+    early_row_weights<PF_ROWS>(a, wA0, pw);
+  } else {
+    early_row_weights<PAIR>(a, wA0, pw);
+    early_row_weights<PAIR>(a, wB0, pw + PAIR);
   }
 }
 
@@ -598,8 +630,13 @@ __device__ __forceinline__ void head_and_slot(int& h, int& slot) {
   }
 }
 
-template <bool NOLSE, int NCH>
+// PAIR: rows of each of a wave's two tokens issued a tile ahead (instantiated
+// with 4, for n <= 4; 0: the first PF_ROWS rows of the first token only).
+template <bool NOLSE, int NCH, int PAIR>
 __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg_per_head) {
+  static_assert(PAIR == 0 || (NCH == 1 && !NOLSE), "both tokens' rows ahead only for n <= 64 with LSEs");
+  constexpr int NPF = PAIR ? 2 * PAIR : PF_ROWS;  // rows in flight across the barrier
+  constexpr int NPRE_A = PAIR ? PAIR : PF_ROWS, NPRE_B = PAIR;
   // two LDS buffers: a wave may merge tile i+1 while others still read tile i
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][LDS_SCALES];
@@ -630,8 +667,8 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   float lA[NCH], lB[NCH];  // raw LSEs of the next tile
   int kA[NCH], kB[NCH];
   float wA[NCH], wB[NCH];  // weights of the current tile
-  uint4 pv[PF_ROWS];       // its first rows, in flight
-  float pw[PF_ROWS];
+  uint4 pv[NPF];           // its first rows, in flight
+  float pw[NPF];
   // The first tile's LSEs and first rows go out together; W_V goes out after
   // them, so that waiting for the LSEs does not wait for W_V (loads complete
   // in issue order), which only the first MFMAs need. Measured on the large
@@ -641,11 +678,15 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   int t0, tend, n0, nend;
   tile_span(ts, 0, t0, tend);
   tile_span(ts, 1, n0, nend);
-  if constexpr (!NOLSE) {
+  if constexpr (NOLSE) {
+    // without LSEs a token's one row is issued a tile ahead, both tokens'
+    issue_rows_early<1>(a, t0 + wave * TOK_PER_WAVE, tend, batch_end, h, lane, pv);
+    issue_rows_early<1>(a, t0 + wave * TOK_PER_WAVE + 1, tend, batch_end, h, lane, pv + 1);
+  } else {
     prefetch_lse<NCH>(a, t0, h, wave, lane, lA, kA, lB, kB);
-    issue_first_rows_early(a, t0, tend, batch_end, h, wave, lane, pv);
+    issue_first_rows_early<PAIR>(a, t0, tend, batch_end, h, wave, lane, pv);
     tile_weights<NCH>(a, t0, tend, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
-    first_row_weights(a, wA[0], pw);
+    first_row_weights<PAIR>(a, wA[0], wB[0], pw);
     prefetch_lse<NCH>(a, n0, h, wave, lane, lA, kA, lB, kB);
   }
   load_wv(a, h, wave, tl, kb, wv, sa);
@@ -667,16 +708,20 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
     const int t_out = min(t0 + tl, a.S - 1);
     const uint2 g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
     if constexpr (NOLSE) {
-      copy_stage(a, tA, ttA, h, lane, liveA, emptyA, codes, scales);
-      copy_stage(a, tB, ttB, h, lane, liveB, emptyB, codes, scales);
+      copy_stage(a, tA, ttA, h, lane, liveA, emptyA, pv[0], codes, scales);
+      copy_stage(a, tB, ttB, h, lane, liveB, emptyB, pv[1], codes, scales);
+      issue_rows_early<1>(a, n0 + wave * TOK_PER_WAVE, nend, batch_end, h, lane, pv);
+      issue_rows_early<1>(a, n0 + wave * TOK_PER_WAVE + 1, nend, batch_end, h, lane, pv + 1);
     } else {
-      merge_stage<NCH, true>(a, tA, ttA, h, lane, liveA, emptyA, wA, pv, pw, codes, scales);
-      merge_stage<NCH, false>(a, tB, ttB, h, lane, liveB, emptyB, wB, pv, pw, codes, scales);
+      // with PAIR > 0 the call has n <= PAIR: every row is among those issued ahead
+      merge_stage<NCH, NPRE_A, PAIR == 0>(a, tA, ttA, h, lane, liveA, emptyA, wA, pv, pw, codes, scales);
+      merge_stage<NCH, NPRE_B, PAIR == 0>(a, tB, ttB, h, lane, liveB, emptyB, wB, pv + NPRE_A, pw + NPRE_A, codes,
+                                           scales);
     }
     if constexpr (!NOLSE) {
       tile_weights<NCH>(a, n0, nend, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
       prefetch_lse<NCH>(a, m0, h, wave, lane, lA, kA, lB, kB);
-      issue_first_rows<NCH>(a, n0, h, wave, lane, wA, pv, pw);
+      issue_next_rows<NCH, PAIR>(a, n0, h, wave, lane, wA, wB, pv, pw);
     }
     // One barrier per tile: it publishes this tile's codes, and since every
     // wave finished the previous tile's MFMAs before merging this one, the
@@ -1054,6 +1099,12 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   p.kernel = MLA_POST_KERNEL_PERSISTENT;
   p.tile_tokens = TILE_T;
   p.lse_chunks = nch;
+  // n <= 4: both tokens' rows a tile ahead (the 8 slots hold all of them).
+  // Measured with 1 to 4 splits: S = 4096 40.1 -> 29.5 us (n = 1), 41.3 ->
+  // 31.2 (n = 2), 45.1 -> 39.4 (n = 4), S = 8192 by 14-30%. Eight rows of
+  // each token for n <= 8 needs 141 registers, one resident workgroup per CU,
+  // and was 20-30% slower with 6 and 8 splits.
+  p.pair_rows = !nolse && nch == 1 && n <= PF_ROWS / 2 ? PF_ROWS / 2 : 0;
   p.workgroups_per_head = wph;
   p.workgroups = NH * wph;
   tile_counts(S, wph, spread_leftover(nolse, n), p.full_tiles, p.short_tokens);
@@ -1082,15 +1133,17 @@ int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t 
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
   const int wph = p.workgroups_per_head;
   if (nolse)
-    hipLaunchKernelGGL((mla_post_kernel<true, 1>), grid, block, 0, stream, k, wph);
+    hipLaunchKernelGGL((mla_post_kernel<true, 1, 0>), grid, block, 0, stream, k, wph);
+  else if (p.pair_rows == PF_ROWS / 2)
+    hipLaunchKernelGGL((mla_post_kernel<false, 1, PF_ROWS / 2>), grid, block, 0, stream, k, wph);
   else if (p.lse_chunks == 1)
-    hipLaunchKernelGGL((mla_post_kernel<false, 1>), grid, block, 0, stream, k, wph);
+    hipLaunchKernelGGL((mla_post_kernel<false, 1, 0>), grid, block, 0, stream, k, wph);
   else if (p.lse_chunks == 2)
-    hipLaunchKernelGGL((mla_post_kernel<false, 2>), grid, block, 0, stream, k, wph);
+    hipLaunchKernelGGL((mla_post_kernel<false, 2, 0>), grid, block, 0, stream, k, wph);
   else if (p.lse_chunks == 4)
-    hipLaunchKernelGGL((mla_post_kernel<false, 4>), grid, block, 0, stream, k, wph);
+    hipLaunchKernelGGL((mla_post_kernel<false, 4, 0>), grid, block, 0, stream, k, wph);
   else
-    hipLaunchKernelGGL((mla_post_kernel<false, 8>), grid, block, 0, stream, k, wph);
+    hipLaunchKernelGGL((mla_post_kernel<false, 8, 0>), grid, block, 0, stream, k, wph);
   return launched(hipGetLastError());
 }
 

@@ -172,6 +172,9 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         # head at 256 CUs): the persistent kernel, with a ragged last tile
         pytest.param(lambda: synth.dense_splits("persistent_ragged", 3, 1030, seed=23, p_neg_inf=0.2), id="persistent_ragged"),
         pytest.param(lambda: synth.single_partial("persistent_no_lse", 1100, seed=24), id="persistent_no_lse"),
+        # n <= 4 on the persistent kernel: both tokens' rows issued a tile ahead
+        pytest.param(lambda: synth.dense_splits("pair_n1", 1, 2100, seed=35, p_neg_inf=0.2), id="persistent_pair_n1"),
+        pytest.param(lambda: synth.dense_splits("pair_n2", 2, 1500, seed=36, p_neg_inf=0.3), id="persistent_pair_n2"),
     ],
 )
 def test_edge(gpu_lib, w):
@@ -183,8 +186,9 @@ def test_edge(gpu_lib, w):
 
 @pytest.mark.parametrize(
     "n,S",
-    [(6, 40), (16, 1100), (20, 70), (66, 20)],
-    ids=["one_tile_instance", "persistent_n16", "persistent_n20", "persistent_two_chunks"],
+    [(6, 40), (16, 1100), (20, 70), (66, 20), (3, 1100), (4, 2100)],
+    ids=["one_tile_instance", "persistent_n16", "persistent_n20", "persistent_two_chunks", "persistent_pair_n3",
+         "persistent_pair_n4"],
 )
 def test_dead_rows_nan_inf_unused(gpu_lib, n, S):
     """Rows of weight 0 hold NaN and inf: the result equals the oracle's, which

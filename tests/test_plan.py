@@ -50,7 +50,7 @@ TABLE = [
     ((8, 128, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=16, workgroups=192)),
     ((8, 256, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=32, workgroups=384)),
     ((16, 4096, True), dict(kernel="persistent", tile_tokens=16, lse_chunks=1, workgroups_per_head=64, workgroups=768,
-                            full_tiles=4, short_tokens=0)),
+                            full_tiles=4, short_tokens=0, pair_rows=0)),
     # one-tile boundaries
     ((16, 512, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16, workgroups_per_head=64, workgroups=768)),
     ((8, 513, True), dict(kernel="one_tile", tile_tokens=16, rows_held=8, workgroups_per_head=33)),
@@ -58,7 +58,11 @@ TABLE = [
     ((1, 1000, False), dict(kernel="one_tile", tile_tokens=16, rows_held=1, workgroups_per_head=63)),
     ((16, 513, True), dict(kernel="persistent", workgroups_per_head=33, full_tiles=0, short_tokens=16)),
     ((17, 64, True), dict(kernel="persistent", workgroups_per_head=4, full_tiles=1, short_tokens=0)),
-    ((1, 1025, False), dict(kernel="persistent", workgroups_per_head=40)),
+    ((1, 1025, False), dict(kernel="persistent", workgroups_per_head=40, pair_rows=0)),
+    # both tokens' rows a tile ahead for n <= 4 with LSEs
+    ((1, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
+    ((4, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
+    ((5, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
     # the one-round rule (65 to 96 tiles) and the leftover deal
     ((16, 1100, True), dict(kernel="persistent", workgroups_per_head=40, workgroups=480, full_tiles=1, short_tokens=12)),
     ((4, 1100, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=1, short_tokens=16)),
@@ -82,9 +86,10 @@ def test_routing_table_at_256_cus(key, expect):
     for field, value in expect.items():
         assert p[field] == value, (field, p)
     if p["kernel"] == "one_tile":
-        assert p["lse_chunks"] == 1 and p["full_tiles"] == 0 and p["short_tokens"] == 0
+        assert p["lse_chunks"] == 1 and p["full_tiles"] == 0 and p["short_tokens"] == 0 and p["pair_rows"] == 0
     else:
         assert p["tile_tokens"] == 16 and p["rows_held"] == 0
+        assert p["pair_rows"] == (4 if key[2] and key[0] <= 4 else 0)
 
 
 def test_empty_batch_launches_nothing():
