@@ -272,7 +272,7 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
     fetch = fk * 1024 * f_scale
     write = wk * 1024 * w_scale
     out = {
-        "kernel": f"mla_post_kernel<false, 1> ({workload} workload)",
+        "kernel": f"mla_post_kernel<false, 1, 0> ({workload} workload)",
         "workload": workload,
         "kernel_source_sha256": kernel_sha(),
         "fetch_kib_per_dispatch": fk,

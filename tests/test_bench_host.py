@@ -62,7 +62,7 @@ def write_counter_csv(path, rows):
 
 def test_traffic_from_counters(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    k = "void (anonymous namespace)::mla_post_kernel<false, 1>(KArgs, int)"
+    k = "void (anonymous namespace)::mla_post_kernel<false, 1, 0>(KArgs, int)"
     other = "at::native::fill"
     # the copy's FETCH_SIZE reads half its bytes, WRITE_SIZE all of them
     write_counter_csv(tmp_path / "f.csv", [(k, 100.0), (k, 104.0), (k, 102.0), (other, 9e9)])
