@@ -1089,7 +1089,9 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
     if (nolse || n <= lat_nmax(tt)) {
       p.kernel = MLA_POST_KERNEL_ONE_TILE;
       p.tile_tokens = tt;
-      p.rows_held = nolse ? 1 : (tt == TILE_T || n <= LAT_NMAX) ? LAT_NMAX : 2 * LAT_NMAX;
+      // rows held per token: the fewest instantiated that hold all n (fewer
+      // registers, so more workgroups resident at once)
+      p.rows_held = nolse ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= LAT_NMAX ? LAT_NMAX : 2 * LAT_NMAX;
       p.lse_chunks = 1;
       p.workgroups_per_head = (S + tt - 1) / tt;
       p.workgroups = NH * p.workgroups_per_head;
@@ -1111,23 +1113,29 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   return p;
 }
 
-template <bool NOLSE>
+template <bool NOLSE, int TT>
 void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
-  if (p.tile_tokens == TILE_T)
-    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T, LAT_NMAX>), grid, block, 0, stream, k);
-  else if (p.rows_held <= LAT_NMAX)
-    hipLaunchKernelGGL((mla_post_latency_kernel<NOLSE, TILE_T / 2, LAT_NMAX>), grid, block, 0, stream, k);
-  else if constexpr (!NOLSE)
-    hipLaunchKernelGGL((mla_post_latency_kernel<false, TILE_T / 2, 2 * LAT_NMAX>), grid, block, 0, stream, k);
+  if constexpr (NOLSE) {
+    hipLaunchKernelGGL((mla_post_latency_kernel<true, TT, LAT_NMAX>), grid, block, 0, stream, k);
+  } else {
+    if (p.rows_held == 2)
+      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, 2>), grid, block, 0, stream, k);
+    else if (p.rows_held == 4)
+      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, 4>), grid, block, 0, stream, k);
+    else if (p.rows_held == LAT_NMAX)
+      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, LAT_NMAX>), grid, block, 0, stream, k);
+    else if constexpr (lat_nmax(TT) > LAT_NMAX)
+      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, 2 * LAT_NMAX>), grid, block, 0, stream, k);
+  }
 }
 
 int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t stream) {
   if (p.kernel == MLA_POST_KERNEL_ONE_TILE) {
-    if (nolse)
-      launch_one_tile<true>(k, p, stream);
+    if (p.tile_tokens == TILE_T)
+      nolse ? launch_one_tile<true, TILE_T>(k, p, stream) : launch_one_tile<false, TILE_T>(k, p, stream);
     else
-      launch_one_tile<false>(k, p, stream);
+      nolse ? launch_one_tile<true, TILE_T / 2>(k, p, stream) : launch_one_tile<false, TILE_T / 2>(k, p, stream);
     return launched(hipGetLastError());
   }
   const dim3 grid((unsigned)p.workgroups), block(THREADS);

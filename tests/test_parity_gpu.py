@@ -167,6 +167,10 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         pytest.param(lambda: synth.dense_splits("latency8_n16", 16, 510, seed=33, p_neg_inf=0.2), id="latency8_n16_S510"),
         pytest.param(lambda: synth.dense_splits("latency16", 4, 900, seed=28, p_neg_inf=0.1), id="latency16_S900"),
         pytest.param(lambda: synth.single_partial("latency16_no_lse", 700, seed=29), id="latency16_no_lse"),
+        # the instances holding 2 and 4 rows per token (n <= 2, n <= 4)
+        pytest.param(lambda: synth.dense_splits("latency16_n2", 2, 777, seed=37, p_neg_inf=0.3), id="latency16_n2"),
+        pytest.param(lambda: synth.dense_splits("latency8_n4", 4, 300, seed=38, p_neg_inf=0.3, p_nan=0.05),
+                     id="latency8_n4"),
         pytest.param(lambda: synth.dense_splits("n16_S800", 16, 800, seed=34, p_neg_inf=0.2), id="n16_persistent_one_tile_each"),
         # S past one device-filling wave of workgroups (more than 64 tiles per
         # head at 256 CUs): the persistent kernel, with a ragged last tile

@@ -40,12 +40,13 @@ def plan(n, S, lse=True, cus=256):
 # (n, S, lse) -> the expected plan at 256 CUs, from the documented rules:
 # one-tile instance while one tile per workgroup fits 64 workgroups per head
 # and the instance holds every row (8-token tiles up to 3 workgroups per CU,
-# i.e. S <= 512, with 16 rows; 16-token tiles with 8 rows); else the
+# i.e. S <= 512, with up to 16 rows; 16-token tiles with up to 8 rows; the
+# fewest of 2, 4, 8, 16 rows that hold n); else the
 # persistent kernel with 64 workgroups per head, 40 from 65 to 96 tiles, and
 # leftover tokens dealt out evenly from n = 6 (whole 16-token tiles below).
 TABLE = [
     # the five standard workloads
-    ((2, 4, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=1, workgroups=12)),
+    ((2, 4, True), dict(kernel="one_tile", tile_tokens=8, rows_held=2, workgroups_per_head=1, workgroups=12)),
     ((1, 64, False), dict(kernel="one_tile", tile_tokens=8, rows_held=1, workgroups_per_head=8, workgroups=96)),
     ((8, 128, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=16, workgroups=192)),
     ((8, 256, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8, workgroups_per_head=32, workgroups=384)),
@@ -54,7 +55,11 @@ TABLE = [
     # one-tile boundaries
     ((16, 512, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16, workgroups_per_head=64, workgroups=768)),
     ((8, 513, True), dict(kernel="one_tile", tile_tokens=16, rows_held=8, workgroups_per_head=33)),
-    ((4, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=8, workgroups_per_head=64)),
+    ((4, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=4, workgroups_per_head=64)),
+    ((1, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=64)),
+    ((3, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=4)),
+    ((5, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8)),
+    ((9, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16)),
     ((1, 1000, False), dict(kernel="one_tile", tile_tokens=16, rows_held=1, workgroups_per_head=63)),
     ((16, 513, True), dict(kernel="persistent", workgroups_per_head=33, full_tiles=0, short_tokens=16)),
     ((17, 64, True), dict(kernel="persistent", workgroups_per_head=4, full_tiles=1, short_tokens=0)),
