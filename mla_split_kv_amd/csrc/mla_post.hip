@@ -69,6 +69,7 @@ constexpr int LDS_OUT = TILE_T * OUT_ROW;      // 4352 B
 constexpr int STORE_LANES = TILE_T * VD * 2 / 16;  // 256 16-byte pieces per output tile
 constexpr int OUT_TILES = 8;                   // output tiles held in LDS before they are written
 constexpr int SPREAD_MIN_N = 6;                // n from which leftover tokens are dealt out evenly
+constexpr int ONE_TILE_SMAX = 1 << 20;         // largest S sent to the one-tile instance beyond its fill
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -1073,8 +1074,8 @@ int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
 
 // The launch for a validated call with S > 0 on a device of `cus` CUs: the
 // one-tile instance when one token tile per workgroup fills the device at
-// most once and the instance can hold every row of a token, else the
-// persistent kernel. mla_post launches exactly this.
+// most once and the instance can hold every row of a token, or when n <= 2
+// with LSEs; else the persistent kernel. mla_post launches exactly this.
 mla_post_plan make_plan(const mla_post_args* a, int cus) {
   mla_post_plan p;
   memset(&p, 0, sizeof(p));
@@ -1084,8 +1085,17 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   const int nch = nolse ? 1 : lse_chunks(n);
   const int ntiles = (S + TILE_T - 1) / TILE_T;
   const int wph = workgroups_per_head(S, cus);
-  if (wph == ntiles && nch == 1) {
-    const int tt = latency_tile(S, cus);
+  // One or two partials with LSEs take the one-tile instance at every size:
+  // a 16-token tile then holds 2 rows per token (59 registers, 4 workgroups
+  // per CU), and the device refills CUs with new workgroups as others end.
+  // Measured against the persistent kernel: one split S = 2048 19.0 -> 15.5
+  // us, 4096 29.4 -> 26.7 us; two splits 2048 19.9 -> 16.9 us, equal at
+  // 8192; with 3 or 4 splits, or without LSEs, it was slower beyond S = 1024.
+  // Up to S = 2^20: a dispatch counts its work-items in 32 bits, and 12
+  // workgroups of 512 per 16 tokens would overflow that past S = 11M.
+  const bool fits = wph == ntiles && nch == 1;
+  if (fits || (!nolse && n <= 2 && S <= ONE_TILE_SMAX)) {
+    const int tt = fits ? latency_tile(S, cus) : TILE_T;
     if (nolse || n <= lat_nmax(tt)) {
       p.kernel = MLA_POST_KERNEL_ONE_TILE;
       p.tile_tokens = tt;

@@ -176,9 +176,12 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         # head at 256 CUs): the persistent kernel, with a ragged last tile
         pytest.param(lambda: synth.dense_splits("persistent_ragged", 3, 1030, seed=23, p_neg_inf=0.2), id="persistent_ragged"),
         pytest.param(lambda: synth.single_partial("persistent_no_lse", 1100, seed=24), id="persistent_no_lse"),
-        # n <= 4 on the persistent kernel: both tokens' rows issued a tile ahead
-        pytest.param(lambda: synth.dense_splits("pair_n1", 1, 2100, seed=35, p_neg_inf=0.2), id="persistent_pair_n1"),
-        pytest.param(lambda: synth.dense_splits("pair_n2", 2, 1500, seed=36, p_neg_inf=0.3), id="persistent_pair_n2"),
+        # one or two partials past S = 1024: the one-tile instance, many rounds
+        pytest.param(lambda: synth.dense_splits("big_n1", 1, 2100, seed=35, p_neg_inf=0.2), id="one_tile_large_n1"),
+        pytest.param(lambda: synth.dense_splits("big_n2", 2, 1500, seed=36, p_neg_inf=0.3), id="one_tile_large_n2"),
+        # 3 or 4 partials past S = 1024: the persistent kernel with both tokens'
+        # rows issued a tile ahead
+        pytest.param(lambda: synth.dense_splits("pair_n3", 3, 2100, seed=39, p_neg_inf=0.2), id="persistent_pair_n3"),
     ],
 )
 def test_edge(gpu_lib, w):

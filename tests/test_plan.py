@@ -65,8 +65,13 @@ TABLE = [
     ((17, 64, True), dict(kernel="persistent", workgroups_per_head=4, full_tiles=1, short_tokens=0)),
     ((1, 1025, False), dict(kernel="persistent", workgroups_per_head=40, pair_rows=0)),
     # both tokens' rows a tile ahead for n <= 4 with LSEs
-    ((1, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
+    ((3, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
     ((4, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
+    # one or two partials with LSEs: the one-tile instance at every size
+    ((1, 4096, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=256)),
+    ((2, 8200, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=513)),
+    ((1, 1 << 20, True), dict(kernel="one_tile", tile_tokens=16, workgroups_per_head=65536)),
+    ((1, (1 << 20) + 16, True), dict(kernel="persistent", workgroups_per_head=64)),
     ((5, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
     # the one-round rule (65 to 96 tiles) and the leftover deal
     ((16, 1100, True), dict(kernel="persistent", workgroups_per_head=40, workgroups=480, full_tiles=1, short_tokens=12)),
@@ -146,6 +151,15 @@ def test_schedule_covers_every_token_once(cus):
             assert 0 <= p["short_tokens"] <= 16
             c = covered(p, int(S))
             assert np.all(c == 1), (n, S, cus, p)
+
+
+def test_grid_fits_a_dispatch():
+    """Every plan's grid, in work-items (512 per workgroup), fits the 32-bit
+    count of a dispatch, up to the largest S the ABI accepts."""
+    for S in (1 << 20, (1 << 20) + 1, 1 << 24, 1 << 30):
+        for n, lse in ((1, True), (2, True), (3, True), (16, True), (1, False), (512, True)):
+            p = plan(n, S, lse)
+            assert p["workgroups"] * 512 < 1 << 32, (n, S, p)
 
 
 def test_current_device_without_gpu_assumes_256():
