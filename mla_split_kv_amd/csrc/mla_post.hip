@@ -41,6 +41,7 @@
 
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <string>
 
@@ -909,26 +910,30 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
 // ---------------------------------------------------------------- stand-alone quantiser
 
 constexpr int QWAVES = 4;
+constexpr int64_t QMAX_BLOCKS = 1 << 16;
 
 __global__ __launch_bounds__(QWAVES * 64) void quantize_kernel(const uint8_t* x, int64_t rows, int cols,
                                                                int64_t xs_bytes, uint8_t* codes, int64_t cs,
                                                                uint8_t* scales, int64_t ss) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6);
-  if (r >= rows) return;  // whole wave
-  for (int c0 = 0; c0 < cols; c0 += 512) {
-    const int c = c0 + lane * 8;
-    const bool in = c < cols;  // cols is a multiple of 32: whole quads are in or out
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (in) {
-      const uint4 v = *reinterpret_cast<const uint4*>(x + r * xs_bytes + (int64_t)c * 2);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    }
-    int code;
-    const uint32_t pk = quant8(w, code);
-    if (in) {
-      *reinterpret_cast<uint32_t*>(codes + r * cs + c / 2) = pk;
-      if ((lane & 3) == 0) scales[r * ss + c / 32] = (uint8_t)code;
+  // a wave per row, striding over the grid (the grid is capped; r is the
+  // same for the whole wave)
+  const int64_t stride = (int64_t)gridDim.x * QWAVES;
+  for (int64_t r = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6); r < rows; r += stride) {
+    for (int c0 = 0; c0 < cols; c0 += 512) {
+      const int c = c0 + lane * 8;
+      const bool in = c < cols;  // cols is a multiple of 32: whole quads are in or out
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (in) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + r * xs_bytes + (int64_t)c * 2);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      }
+      int code;
+      const uint32_t pk = quant8(w, code);
+      if (in) {
+        *reinterpret_cast<uint32_t*>(codes + r * cs + c / 2) = pk;
+        if ((lane & 3) == 0) scales[r * ss + c / 32] = (uint8_t)code;
+      }
     }
   }
 }
@@ -1239,8 +1244,9 @@ int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stri
       !span_ok(rows, c_stride, 1, 0, 1, 0, cols / 2) ||
       !span_ok(rows, s_stride, 1, 0, 1, 0, cols / 32))
     return MLA_POST_ERANGE;
-  const int64_t blocks = (rows + QWAVES - 1) / QWAVES;
-  if (blocks > 0x7FFFFFFF) return MLA_POST_ERANGE;
+  // at most 2^16 workgroups, each wave striding over the rows: the grid's
+  // work-item count must fit the 32 bits of a dispatch
+  const int64_t blocks = std::min<int64_t>((rows + QWAVES - 1) / QWAVES, QMAX_BLOCKS);
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint8_t*>(x), rows, cols, x_stride * 2, codes, c_stride, scales, s_stride);
   return launched(hipGetLastError());

@@ -355,6 +355,20 @@ def test_quantizer_exhaustive(gpu_lib):
     assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
 
 
+def test_quantizer_rows_past_one_grid(gpu_lib):
+    """More rows than one pass of the quantiser's capped grid (2^16
+    workgroups of 4 rows): every wave strides on, and all 300,000 rows equal
+    the oracle's encoding, bit for bit."""
+    m = gpu_lib
+    say("quantiser 300k rows")
+    rng = np.random.default_rng(31)
+    x = O.rne_bf16(rng.standard_normal((300000, 32)) * 3.0)
+    codes, scales = m.quantize_mxfp4(bf16_to_dev(x, "cuda"))
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_mxfp4(x)
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+
+
 def test_quantizer_wv_matches_oracle(gpu_lib):
     """W_V put into MXFP4 on the GPU equals the oracle's encoding."""
     m = gpu_lib
