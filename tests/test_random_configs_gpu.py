@@ -36,9 +36,10 @@ def say(msg):
 def draw_S(rng) -> int:
     """Token counts on both sides of the routing boundaries at 256 CUs:
     8-token tiles up to 512, 16-token tiles or the persistent kernel up to
-    1024, several tiles per workgroup past it."""
-    band = rng.choice(4, p=[0.3, 0.3, 0.2, 0.2])
-    lo, hi = [(1, 64), (65, 512), (513, 1024), (1025, 1400)][band]
+    1024, 40 workgroups per head up to 1536, 64 and several tiles each past
+    it (and the one-tile instance at any size for one or two partials)."""
+    band = rng.choice(5, p=[0.25, 0.25, 0.2, 0.15, 0.15])
+    lo, hi = [(1, 64), (65, 512), (513, 1024), (1025, 1536), (1537, 2100)][band]
     return int(rng.integers(lo, hi + 1))
 
 
