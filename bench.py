@@ -134,6 +134,34 @@ def time_per_call(call, calls: int, torch, scratch=None) -> float:
     return statistics.median(out)
 
 
+def time_graph(call, torch, per_graph: int = 100, replays: int = 20) -> float:
+    """Microseconds per call when `per_graph` calls are captured in one HIP
+    graph and the graph is replayed back to back (no host launch per call).
+    The library records no memset in a capture; each replay is checked by the
+    graph tests, not here."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return 1e3 * ev0.elapsed_time(ev1) / (replays * per_graph)
+
+
 def copy_ceiling(torch) -> float:
     """Device copy rate (GB/s, bytes read + bytes written) of a plain 1 GiB
     copy: the stream-copy ceiling the kernel is also compared with."""
@@ -443,6 +471,7 @@ def main() -> int:
                 "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "tokens_per_s": round(wk.S / (us * 1e-6), 1),
                 "us_single_warm": round(time_per_call(ck, 200, torch), 3),
+                "us_per_call_graph": round(time_graph(ck, torch), 3),
                 "us_single_cold": round(time_per_call(ck, 100, torch, scratch), 3),
                 "alg_bytes": ak["alg_bytes"],
             }
