@@ -15,6 +15,7 @@
 #include "mla_post.h"
 
 #define FIELD(name) printf("offset %s %zu\n", #name, offsetof(mla_post_args, name))
+#define PFIELD(name) printf("plan_offset %s %zu\n", #name, offsetof(mla_post_plan, name))
 
 static mla_post_args good(int n, int S) {
   mla_post_args a;
@@ -92,5 +93,22 @@ int main(void) {
                                                  (uint8_t*)(uintptr_t)0x200000, 32,
                                                  (uint8_t*)(uintptr_t)0x300000, 2, NULL));
   printf("last_hip_error '%s'\n", mla_post_last_hip_error());
+
+  /* the launch plan, for 256 CUs (host only) */
+  {
+    mla_post_plan p;
+    printf("plan_sizeof %zu\n", sizeof(mla_post_plan));
+    PFIELD(kernel); PFIELD(tile_tokens); PFIELD(rows_held); PFIELD(lse_chunks); PFIELD(workgroups_per_head);
+    PFIELD(workgroups); PFIELD(full_tiles); PFIELD(short_tokens); PFIELD(pair_rows); PFIELD(cus);
+    a = good(16, 4096);
+    status("plan_large", mla_post_plan_for(&a, 256, &p));
+    printf("plan_large %d %d %d %d\n", p.kernel, p.workgroups, p.full_tiles, p.cus);
+    a = good(2, 4);
+    status("plan_tiny", mla_post_plan_for(&a, 256, &p));
+    printf("plan_tiny %d %d %d %d\n", p.kernel, p.tile_tokens, p.rows_held, p.workgroups);
+    a = good(4, 8); a.o_st = 6143;
+    status("plan_bad_stride", mla_post_plan_for(&a, 256, &p));
+    status("plan_null_out", mla_post_plan_for(&a, 256, NULL));
+  }
   return 0;
 }

@@ -61,9 +61,13 @@ def probe_output(tmp_path_factory):
         parts = line.split()
         if parts[0] == "offset":
             offsets[parts[1]] = int(parts[2])
+        elif parts[0] == "plan_offset":
+            offsets["plan." + parts[1]] = int(parts[2])
+        elif parts[0] in ("plan_large", "plan_tiny") and parts[1].lstrip("-").isdigit():
+            sizes[parts[0]] = [int(x) for x in parts[1:]]
         elif parts[0] == "status":
             statuses[parts[1]] = int(parts[2])
-        elif parts[0] in ("sizeof", "v1_size", "header_version", "library_version"):
+        elif parts[0] in ("sizeof", "v1_size", "header_version", "library_version", "plan_sizeof"):
             sizes[parts[0]] = int(parts[1])
     return sizes, offsets, statuses
 
@@ -72,7 +76,21 @@ def test_struct_layout_matches_binding(probe_output):
     sizes, offsets, _ = probe_output
     assert sizes["sizeof"] == ctypes.sizeof(m.MlaPostArgs) == 224
     assert sizes["v1_size"] == m.ARGS_V1_SIZE == offsets["q"]
-    assert offsets == {name: getattr(m.MlaPostArgs, name).offset for name, _ in m.MlaPostArgs._fields_}
+    args_offsets = {k: v for k, v in offsets.items() if not k.startswith("plan.")}
+    assert args_offsets == {name: getattr(m.MlaPostArgs, name).offset for name, _ in m.MlaPostArgs._fields_}
+
+
+def test_plan_from_c(probe_output):
+    """mla_post_plan as C sees it matches the binding's struct, and the plan
+    query gives from C what it gives from Python (256 CUs)."""
+    sizes, offsets, statuses = probe_output
+    assert sizes["plan_sizeof"] == ctypes.sizeof(m.MlaPostPlan) == 40
+    plan_offsets = {k[5:]: v for k, v in offsets.items() if k.startswith("plan.")}
+    assert plan_offsets == {name: getattr(m.MlaPostPlan, name).offset for name, _ in m.MlaPostPlan._fields_}
+    assert statuses["plan_large"] == statuses["plan_tiny"] == OK
+    assert sizes["plan_large"] == [2, 768, 4, 256]  # persistent, 768 workgroups, 4 full tiles each
+    assert sizes["plan_tiny"] == [1, 8, 2, 12]      # one-tile, 8-token tiles, 2 rows, 12 workgroups
+    assert statuses["plan_bad_stride"] == ESTRIDE and statuses["plan_null_out"] == EINVAL
 
 
 def test_versions_agree(probe_output):
@@ -82,4 +100,4 @@ def test_versions_agree(probe_output):
 
 def test_status_codes_from_c(probe_output):
     _, _, statuses = probe_output
-    assert statuses == EXPECTED
+    assert {k: v for k, v in statuses.items() if not k.startswith("plan_")} == EXPECTED
