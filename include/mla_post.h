@@ -139,12 +139,16 @@ int mla_post_check(const mla_post_args* a);
 #define MLA_POST_KERNEL_NONE 0       /* S == 0: nothing is launched */
 #define MLA_POST_KERNEL_ONE_TILE 1   /* one token tile per workgroup, every load issued up front */
 #define MLA_POST_KERNEL_PERSISTENT 2 /* workgroups that each keep one head and walk its tiles */
+#define MLA_POST_KERNEL_SPLIT_ROWS 3 /* one small token tile per workgroup, 8 / tile_tokens waves sharing the
+                                        partials of each token (many partials, few tokens) */
 
 typedef struct mla_post_plan {
   int32_t kernel;              /* MLA_POST_KERNEL_* */
-  int32_t tile_tokens;         /* tokens of a full tile: 8 or 16 */
-  int32_t rows_held;           /* one-tile kernel: partial rows per token held at once (8 or 16); else 0 */
-  int32_t lse_chunks;          /* persistent kernel: 64-lane chunks of partials per token (1, 2, 4 or 8); else 1 */
+  int32_t tile_tokens;         /* tokens of a full tile: 8 or 16 (split-rows kernel: 1, 2 or 4) */
+  int32_t rows_held;           /* one-tile kernel: partial rows per token held at once (1, 2, 4, 8 or 16);
+                                  split-rows kernel: rows each wave holds at once (8 or 16); else 0 */
+  int32_t lse_chunks;          /* persistent and split-rows kernels: 64-lane chunks of partials per token
+                                  (1, 2, 4 or 8); else 1 */
   int32_t workgroups_per_head; /* the grid is 12 times this */
   int32_t workgroups;          /* grid size (workgroups of 512 threads) */
   int32_t full_tiles;          /* persistent kernel: full 16-token tiles of every workgroup */

@@ -773,6 +773,54 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
 
 // ---------------------------------------------------------------- the latency-regime kernel
 
+// The output piece a thread of a one-tile workgroup writes: token tok of the
+// tile (thread / 16), columns col .. col + 7 of head h's 128, and the gate
+// values of those columns, loaded at once (a thread whose token lies past S
+// or past the tile's TT tokens loads and stores nothing).
+struct OutPiece {
+  int tok, col;
+  bool live;
+  int64_t off;  // byte offset in gate and core
+  uint4 g8;
+};
+
+__device__ __forceinline__ OutPiece out_piece(const KArgs& a, int h, int t0, int tt) {
+  OutPiece o;
+  o.tok = threadIdx.x >> 4;
+  o.col = (threadIdx.x & 15) * 8;
+  const int t = t0 + o.tok;
+  o.live = o.tok < tt && t < a.S;
+  o.off = ((int64_t)t * GROWS + h * VD + o.col) * 2;
+  o.g8 = make_uint4(0u, 0u, 0u, 0u);
+  if (o.live) o.g8 = load_nt16(a.gate + o.off);
+  return o;
+}
+
+// The tile's MXFP4 latents in LDS (after a barrier) times this wave's 16 rows
+// of W_V[h] (wv, sa) -> bf16 -> s_out; after a barrier each thread with a
+// live output piece writes bf16(that * gate) to core.
+__device__ __forceinline__ void tile_wuv_store(const KArgs& a, int wave, int tl, int kb, const uint4 wv[4], int sa,
+                                               const uint8_t* s_codes, const uint8_t* s_scales, uint8_t* s_out,
+                                               const OutPiece& out) {
+  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const uint8_t* brow = s_codes + tl * 16;
+    acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
+  }
+  asm volatile("" : "+v"(acc));  // MFMAs with the whole wave active (see the main kernel)
+  *reinterpret_cast<uint2*>(s_out + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
+      make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+  __syncthreads();
+  if (out.live) {
+    const uint4 av = *reinterpret_cast<const uint4*>(s_out + out.tok * OUT_ROW + out.col * 2);
+    store_nt16(a.core + out.off, gate_mul(av, out.g8));
+  }
+}
+
 // When the whole grid is resident at once (one token tile per workgroup) and
 // n <= lat_nmax(TT), bandwidth is not the bound; the chain of dependent memory
 // round trips is (LSEs -> weights -> rows of one token -> rows of the other
@@ -813,13 +861,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
   uint4 wv[4];
   int sa = 0;
   load_wv(a, h, wave, tl, kb, wv, sa);
-  // the gate piece this thread writes at the end (token i / 16, 8 columns)
-  const int tok = threadIdx.x >> 4, col = (threadIdx.x & 15) * 8;
-  const int t_out = t0 + tok;
-  const bool out_live = tok < TT && t_out < a.S;
-  const int64_t out_off = ((int64_t)t_out * GROWS + h * VD + col) * 2;
-  uint4 g8 = make_uint4(0u, 0u, 0u, 0u);
-  if (out_live) g8 = load_nt16(a.gate + out_off);
+  const OutPiece out = out_piece(a, h, t0, TT);
 
   const int ttA = wave, ttB = wave + WAVES;
   const int tA = t0 + ttA, tB = t0 + ttB;
@@ -887,24 +929,133 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
   quant_to_lds(a, tA, ttA, h, lane, liveA, latA, s_codes, s_scales);
   quant_to_lds(a, tB, ttB, h, lane, liveB, latB, s_codes, s_scales);
   __syncthreads();
+  tile_wuv_store(a, wave, tl, kb, wv, sa, s_codes, s_scales, s_out, out);
+}
 
-  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  {
-    const uint8_t* brow = s_codes + tl * 16;
-    acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
-    acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
-    acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
-    acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
+// ---------------------------------------------------------------- the split-rows kernel
+
+// Many partials and few tokens (a long context split many ways in a small
+// decode batch): the other kernels give each wave whole tokens, so a wave
+// walks a token's n rows in sequence while the grid holds few workgroups.
+// Here G waves share each token: a workgroup takes TT = 8 / G tokens of one
+// head, and wave w takes token w / G and its partials j = g, g + G, g + 2G,
+// .. (g = w mod G). The LSEs, the first SPLIT_RB (at most) of those rows, W_V
+// and the gate are all issued before anything waits; further rows stream
+// through the same registers, each issued as the row before it in its
+// register is summed. A wave sums its rows in that order (skipping weight-0 rows as
+// the other kernels do); the G sums of a token are then added in LDS in the
+// order g = 0, 1, .., G - 1. So the order of summation differs from the other
+// kernels' j = 0, 1, .., n - 1 (the merge admits any order; the float32
+// rounding stays within the same bound) and is fixed, so results repeat.
+constexpr int SPLIT_RB = 16;  // rows a wave holds at once
+
+// Zero codes for tile slot tt, whose token does not exist (an MFMA column of
+// zeros, never stored).
+__device__ __forceinline__ void empty_slot(const KArgs& a, int tt, int h, int lane, uint8_t* s_codes,
+                                           uint8_t* s_scales) {
+  const uint32_t zero[4] = {0u, 0u, 0u, 0u};
+  quant_to_lds(a, 0, tt, h, lane, false, zero, s_codes, s_scales);
+}
+
+template <int G, int NCH>
+__global__ __launch_bounds__(THREADS) void mla_post_split_kernel(const KArgs a) {
+  static_assert(G == 2 || G == 4 || G == 8, "waves per token");
+  constexpr int TT = WAVES / G;
+  constexpr int RMAX = 64 * NCH / G;                    // most rows of one wave (n <= 64 NCH)
+  constexpr int RB = RMAX < SPLIT_RB ? RMAX : SPLIT_RB;  // rows held at once
+  constexpr int NB = RMAX / RB;                         // batches of RB rows
+  constexpr int NRED = WAVES - TT;                      // waves whose sums go through LDS
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[LDS_OUT];
+  __shared__ __attribute__((aligned(16))) float4 s_red[NRED][2][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x % NH;
+  const int t0 = (blockIdx.x / NH) * TT;
+  const int tl = lane & 15, kb = lane >> 4;
+  const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
+  const int tt = wave / G, g = wave % G;
+  const int t = t0 + tt;
+  const bool live = t < a.S;
+  const bool use = live && t < batch_end;
+  // rows of this wave: j = g + G i for i < mine
+  const int mine = use ? (a.n - g + G - 1) / G : 0;
+  const uint8_t* base = row_base(a, use ? t : 0, h);
+  const int64_t step = (int64_t)G * a.o_sj;
+
+  float l[NCH];
+  int kv[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    l[c] = -INFINITY;
+    kv[c] = 1;
   }
-  asm volatile("" : "+v"(acc));  // MFMAs with the whole wave active (see the main kernel)
-  *reinterpret_cast<uint2*>(s_out + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
-      make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+  if (use) issue_lse<NCH>(a, t, h, lane, l, kv);
+  // row i of this wave through a buffer resource of 1 KiB, or of 0 bytes
+  // (zeros, no memory access) when the wave has no row i
+  auto row = [&](int i) {
+    const uint8_t* p = base + (int64_t)g * a.o_sj + (int64_t)i * step;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(i < mine ? p : base), (short)0, i < mine ? KVL * 2 : 0, BUF_WORD3);
+    const v4u x = (v4u)__builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, NT_ROWS ? 2 : 0);  // 2: nt
+    return make_uint4(x.x, x.y, x.z, x.w);
+  };
+  uint4 v[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) v[i] = row(i);
+
+  uint4 wv[4];
+  int sa = 0;
+  load_wv(a, h, wave, tl, kb, wv, sa);
+  const OutPiece out = out_piece(a, h, t0, TT);
+  // slots past the tile's tokens: zero codes
+#pragma unroll
+  for (int e = TT + wave; e < TILE_T; e += WAVES) empty_slot(a, e, h, lane, s_codes, s_scales);
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (use) {
+    finish_lse<NCH>(a, lane, l, kv);
+    lse_to_weights<NCH>(l);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b == 0 || b * RB < mine) {
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+          const int i = b * RB + k;
+          // partial j = g + G i: chunk (G i) / 64 (g < G and G divides 64), lane j mod 64
+          const int wb = i < mine ? __builtin_amdgcn_readlane(__float_as_int(l[(G * i) >> 6]), (g + G * i) & 63) : 0;
+          if (wb & 0x7FFFFFFF) fma_row(__int_as_float(wb), v[k], acc);
+          if (b + 1 < NB) v[k] = row(i + RB);
+        }
+      }
+    }
+  }
+  // the G sums of each token: waves g > 0 hand theirs to wave g = 0
+  if (g > 0) {
+    float4* r = s_red[tt * (G - 1) + g - 1][0];
+    r[lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    r[64 + lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
   __syncthreads();
-  if (out_live) {
-    const uint4 av = *reinterpret_cast<const uint4*>(s_out + tok * OUT_ROW + col * 2);
-    store_nt16(a.core + out_off, gate_mul(av, g8));
+  if (g == 0) {
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+      const float4* r = s_red[tt * (G - 1) + k - 1][0];
+      const float4 x = r[lane], y = r[64 + lane];
+      acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+      acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+    }
+    uint32_t lat[4] = {0u, 0u, 0u, 0u};
+    if (use) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lat[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
+    }
+    quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
   }
+  __syncthreads();
+  tile_wuv_store(a, wave, tl, kb, wv, sa, s_codes, s_scales, s_out, out);
 }
 
 // ---------------------------------------------------------------- stand-alone quantiser
@@ -1077,6 +1228,26 @@ int latency_tile(int S, int cus) {
 // 64-lane LSE chunks the persistent kernel is instantiated for.
 int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
 
+// Tokens per workgroup of the split-rows kernel for a call with LSEs, or 0
+// when the call does not take it: more partials than the one-tile instance
+// holds, and at most half as many 16-token tiles as CUs (S <= 160 at 256
+// CUs). The tile is the largest (4, 2 or 1 tokens) whose waves hold at most
+// two batches of rows, made smaller while the grid stays within one
+// workgroup per CU. Measured at 256 CUs against the persistent kernel, 17 to
+// 512 splits: S = 16 10.8 -> 5.3 us (17 splits), 25.0 -> 5.9 (64), 171.6 ->
+// 21.9 (512); S = 160 13.1 -> 11.1 (17), 29.5 -> 22.7 (64), 212.8 -> 177.5
+// (512). At S = 192 the persistent kernel is 9-18% faster with 17 to 32
+// splits, within 2% from 33 to 96, 4-6% slower from 128; at S = 256 it is
+// faster by 3-23%.
+int split_tile(int n, int S, int cus) {
+  const int64_t ntiles = (S + TILE_T - 1) / TILE_T;
+  if (n <= 2 * LAT_NMAX || 2 * NH * ntiles > cus) return 0;
+  int tt = 4;
+  while (tt > 1 && tt * n > 2 * WAVES * SPLIT_RB) tt /= 2;
+  while (tt > 1 && (int64_t)NH * ((S + tt / 2 - 1) / (tt / 2)) <= cus) tt /= 2;
+  return tt;
+}
+
 // The launch for a validated call with S > 0 on a device of `cus` CUs: the
 // one-tile instance when one token tile per workgroup fills the device at
 // most once and the instance can hold every row of a token, or when n <= 2
@@ -1113,6 +1284,16 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
       return p;
     }
   }
+  const int stt = nolse ? 0 : split_tile(n, S, cus);
+  if (stt > 0) {
+    p.kernel = MLA_POST_KERNEL_SPLIT_ROWS;
+    p.tile_tokens = stt;
+    p.lse_chunks = stt == 1 ? nch : n <= 64 ? 1 : 2;
+    p.rows_held = min(SPLIT_RB, 64 * p.lse_chunks * stt / WAVES);
+    p.workgroups_per_head = (S + stt - 1) / stt;
+    p.workgroups = NH * p.workgroups_per_head;
+    return p;
+  }
   p.kernel = MLA_POST_KERNEL_PERSISTENT;
   p.tile_tokens = TILE_T;
   p.lse_chunks = nch;
@@ -1145,7 +1326,28 @@ void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream)
   }
 }
 
+template <int G, int NCH>
+void launch_split(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_post_split_kernel<G, NCH>), dim3((unsigned)p.workgroups), dim3(THREADS), 0, stream, k);
+}
+
 int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t stream) {
+  if (p.kernel == MLA_POST_KERNEL_SPLIT_ROWS) {
+    const int c = p.lse_chunks;
+    if (p.tile_tokens == 4)
+      launch_split<2, 1>(k, p, stream);
+    else if (p.tile_tokens == 2)
+      c == 1 ? launch_split<4, 1>(k, p, stream) : launch_split<4, 2>(k, p, stream);
+    else if (c == 1)
+      launch_split<8, 1>(k, p, stream);
+    else if (c == 2)
+      launch_split<8, 2>(k, p, stream);
+    else if (c == 4)
+      launch_split<8, 4>(k, p, stream);
+    else
+      launch_split<8, 8>(k, p, stream);
+    return launched(hipGetLastError());
+  }
   if (p.kernel == MLA_POST_KERNEL_ONE_TILE) {
     if (p.tile_tokens == TILE_T)
       nolse ? launch_one_tile<true, TILE_T>(k, p, stream) : launch_one_tile<false, TILE_T>(k, p, stream);

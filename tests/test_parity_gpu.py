@@ -100,6 +100,10 @@ def test_large_decode_sampled(gpu_lib):
         # more than 8 tiles per workgroup (S > 8 x 64 x 16): the staged output
         # is written after 8 tiles and its buffers reused for the rest
         pytest.param(lambda: synth.dense_splits("persistent_long", 2, 9000, seed=27, p_neg_inf=0.1), id="n2_S9000"),
+        # 4 and 8 LSE chunks in the persistent kernel (with fewer tokens these
+        # many splits take the split-rows kernel)
+        pytest.param(lambda: synth.dense_splits("persistent_n129", 129, 340, seed=44, p_neg_inf=0.2), id="n129_S340"),
+        pytest.param(lambda: synth.dense_splits("persistent_n257", 257, 340, seed=45, p_neg_inf=0.3), id="n257_S340"),
     ],
 )
 def test_persistent_multi_tile_sampled(gpu_lib, make):
@@ -152,6 +156,8 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         pytest.param(lambda: synth.dense_splits("n1_with_lse", 1, 19, seed=13, p_neg_inf=0.3, p_nan=0.1, p_pos_inf=0.1), id="n1_lse"),
         # 16 splits on 8-token tiles: the one-tile instance holding 16 rows per token
         pytest.param(lambda: synth.dense_splits("n16_small", 16, 50, seed=31, p_neg_inf=0.2), id="n16_one_tile"),
+        # more than 64 splits and few tokens: the split-rows kernel, one token
+        # per workgroup, 2, 4 and 8 LSE chunks
         pytest.param(lambda: synth.dense_splits("n65", 65, 9, seed=11, p_neg_inf=0.1), id="n65_two_chunks"),
         pytest.param(lambda: synth.dense_splits("n200", 200, 5, seed=30, p_neg_inf=0.3), id="n200_four_chunks"),
         pytest.param(lambda: synth.dense_splits("n300", 300, 3, seed=12, p_neg_inf=0.5), id="n300_eight_chunks"),
@@ -193,16 +199,17 @@ def test_edge(gpu_lib, w):
 
 @pytest.mark.parametrize(
     "n,S",
-    [(6, 40), (16, 1100), (20, 70), (66, 20), (3, 1100), (4, 2100)],
+    [(6, 40), (16, 1100), (20, 400), (66, 340), (3, 1100), (4, 2100), (24, 150), (20, 40), (66, 20)],
     ids=["one_tile_instance", "persistent_n16", "persistent_n20", "persistent_two_chunks", "persistent_pair_n3",
-         "persistent_pair_n4"],
+         "persistent_pair_n4", "split_rows_tile4", "split_rows_tile2", "split_rows_two_chunks"],
 )
 def test_dead_rows_nan_inf_unused(gpu_lib, n, S):
     """Rows of weight 0 hold NaN and inf: the result equals the oracle's, which
     never touches them, and is finite. Both kernels load some such rows before
     their weights are known (the one-tile instance all of its rows, the
     persistent kernel the first 8 rows of each workgroup's first tile) and
-    must leave them out of the sum."""
+    must leave them out of the sum (the split-rows kernel too: it loads every
+    row of its tokens up front)."""
     w = synth.dense_splits(f"poisoned_dead_n{n}", n, S, seed=20, p_neg_inf=0.2, p_nan=0.1, p_pos_inf=0.1)
     lse = w.lse_view()
     dead = ~np.isfinite(lse)
@@ -213,14 +220,51 @@ def test_dead_rows_nan_inf_unused(gpu_lib, n, S):
     assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
 
 
-@pytest.mark.parametrize("n", [4, 20], ids=["one_tile_instance", "persistent"])
-def test_strided_weights_and_lse(gpu_lib, n):
+# (n, S, tokens per workgroup the plan gives at 256 CUs, workload options)
+SPLIT_ROWS = [
+    # 2 waves per token (4-token tiles): rows j = g, g + 2, ..; a ragged last
+    # tile; with more than 32 splits a second batch of rows per wave
+    (20, 157, 4, dict(p_neg_inf=0.2)),
+    (32, 99, 4, dict(p_neg_inf=0.3, p_nan=0.05)),
+    (33, 64, 4, dict(p_neg_inf=0.1)),
+    (64, 43, 4, dict(p_neg_inf=0.05, p_pos_inf=0.05)),
+    # 4 waves per token (2-token tiles): n not a multiple of 4; 2 LSE chunks
+    # and two batches of rows per wave
+    (40, 33, 2, dict(p_neg_inf=0.1)),
+    (100, 61, 2, dict(p_neg_inf=0.2)),
+    # 8 waves per token, one token per workgroup: 1, 2, 4 and 8 LSE chunks;
+    # with 129 and more splits a wave streams further batches of rows
+    (50, 10, 1, dict(p_neg_inf=0.2)),
+    (100, 7, 1, dict(p_neg_inf=0.1)),
+    (129, 3, 1, dict(p_neg_inf=0.1)),
+    (300, 2, 1, dict(p_neg_inf=0.4, p_nan=0.05)),
+    (512, 1, 1, dict(p_neg_inf=0.02)),
+    # tokens all of whose partials are dead: exact zeros
+    (24, 150, 4, dict(p_neg_inf=0.9)),
+]
+
+
+@pytest.mark.parametrize("n,S,tt,opts", SPLIT_ROWS, ids=[f"n{n}_S{S}_tile{tt}" for n, S, tt, _ in SPLIT_ROWS])
+def test_split_rows(gpu_lib, n, S, tt, opts):
+    """The split-rows kernel (several waves per token, each summing every
+    G-th partial, the sums added in LDS): the plan takes it with the expected
+    tile, and every token meets T1-T4 against the oracle."""
+    m = gpu_lib
+    w = synth.dense_splits(f"split_rows_n{n}_S{S}", n, S, seed=100 + n, **opts)
+    d = device_inputs(w)
+    p = m.plan(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"])
+    assert p["kernel"] == "split_rows" and p["tile_tokens"] == tt, p
+    full_parity(m, w)
+
+
+@pytest.mark.parametrize("n,S", [(4, 33), (20, 33), (20, 400)], ids=["one_tile_instance", "split_rows", "persistent"])
+def test_strided_weights_and_lse(gpu_lib, n, S):
     """W_V codes as a column slice of a wider buffer, scales stored with the
     block axis outermost, lse as a non-dense view: same result as the dense
-    layout, and equal to the oracle (4 splits: the one-tile instance; 20: the
-    persistent kernel)."""
+    layout, and equal to the oracle (4 splits: the one-tile instance; 20
+    splits: the split-rows kernel at S = 33, the persistent one at 400)."""
     m = gpu_lib
-    w = synth.dense_splits("strided", n, 33, seed=21, p_neg_inf=0.1)
+    w = synth.dense_splits("strided", n, S, seed=21, p_neg_inf=0.1)
     d = device_inputs(w)
     base = run_debug(m, d)
     wide = torch.zeros((12, 128, 512), dtype=torch.uint8, device="cuda")
@@ -228,7 +272,7 @@ def test_strided_weights_and_lse(gpu_lib, n):
     w_v = wide[:, :, 128:384]
     sc_t = d["w_v_scale"].permute(2, 0, 1).contiguous()  # [16, 12, 128]
     w_s = sc_t.permute(1, 2, 0)  # logical [12, 128, 16], strides (128, 1, 1536)
-    lse_wide = torch.full((n, 33, 12, 3), float("nan"), device="cuda")
+    lse_wide = torch.full((n, S, 12, 3), float("nan"), device="cuda")
     lse_wide[..., 1] = d["lse"]
     lse_v = lse_wide[..., 1]
     say("strided: w_v slice, scales block-major, lse stride 3")

@@ -41,9 +41,11 @@ def plan(n, S, lse=True, cus=256):
 # one-tile instance while one tile per workgroup fits 64 workgroups per head
 # and the instance holds every row (8-token tiles up to 3 workgroups per CU,
 # i.e. S <= 512, with up to 16 rows; 16-token tiles with up to 8 rows; the
-# fewest of 2, 4, 8, 16 rows that hold n); else the
-# persistent kernel with 64 workgroups per head, 40 from 65 to 96 tiles, and
-# leftover tokens dealt out evenly from n = 6 (whole 16-token tiles below).
+# fewest of 2, 4, 8, 16 rows that hold n); the split-rows kernel for more
+# than 16 partials with LSEs up to S = 160 (4-, 2- or 1-token tiles); else
+# the persistent kernel with 64 workgroups per head, 40 from 65 to 96 tiles,
+# and leftover tokens dealt out evenly from n = 6 (whole 16-token tiles
+# below).
 TABLE = [
     # the five standard workloads
     ((2, 4, True), dict(kernel="one_tile", tile_tokens=8, rows_held=2, workgroups_per_head=1, workgroups=12)),
@@ -62,7 +64,7 @@ TABLE = [
     ((9, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16)),
     ((1, 1000, False), dict(kernel="one_tile", tile_tokens=16, rows_held=1, workgroups_per_head=63)),
     ((16, 513, True), dict(kernel="persistent", workgroups_per_head=33, full_tiles=0, short_tokens=16)),
-    ((17, 64, True), dict(kernel="persistent", workgroups_per_head=4, full_tiles=1, short_tokens=0)),
+    ((17, 161, True), dict(kernel="persistent", workgroups_per_head=11, full_tiles=0, short_tokens=15)),
     ((1, 1025, False), dict(kernel="persistent", workgroups_per_head=40, pair_rows=0)),
     # both tokens' rows a tile ahead for n <= 4 with LSEs
     ((3, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
@@ -82,10 +84,26 @@ TABLE = [
     ((5, 4112, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=4, short_tokens=16)),
     ((16, 9000, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=8, short_tokens=13)),
     # LSE chunks
-    ((64, 100, True), dict(kernel="persistent", lse_chunks=1)),
-    ((65, 100, True), dict(kernel="persistent", lse_chunks=2)),
-    ((200, 100, True), dict(kernel="persistent", lse_chunks=4)),
-    ((512, 2, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=1)),
+    ((64, 400, True), dict(kernel="persistent", lse_chunks=1)),
+    ((65, 400, True), dict(kernel="persistent", lse_chunks=2)),
+    ((200, 400, True), dict(kernel="persistent", lse_chunks=4)),
+    ((512, 400, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=25)),
+    # the split-rows kernel: the largest tile whose waves hold at most two
+    # batches of 16 rows (4 tokens up to 64 splits, 2 up to 128, else 1),
+    # smaller while the grid stays within one workgroup per CU
+    ((17, 64, True), dict(kernel="split_rows", tile_tokens=4, rows_held=16, lse_chunks=1, workgroups_per_head=16,
+                          workgroups=192)),
+    ((17, 16, True), dict(kernel="split_rows", tile_tokens=1, rows_held=8, workgroups_per_head=16)),
+    ((17, 32, True), dict(kernel="split_rows", tile_tokens=2, rows_held=16, workgroups_per_head=16)),
+    ((64, 160, True), dict(kernel="split_rows", tile_tokens=4, lse_chunks=1, workgroups_per_head=40, workgroups=480)),
+    ((64, 100, True), dict(kernel="split_rows", tile_tokens=4, lse_chunks=1)),
+    ((65, 100, True), dict(kernel="split_rows", tile_tokens=2, rows_held=16, lse_chunks=2, workgroups_per_head=50)),
+    ((128, 7, True), dict(kernel="split_rows", tile_tokens=1, lse_chunks=2, workgroups_per_head=7, workgroups=84)),
+    ((129, 100, True), dict(kernel="split_rows", tile_tokens=1, rows_held=16, lse_chunks=4)),
+    ((200, 5, True), dict(kernel="split_rows", tile_tokens=1, lse_chunks=4)),
+    ((512, 2, True), dict(kernel="split_rows", tile_tokens=1, rows_held=16, lse_chunks=8, workgroups_per_head=2,
+                          workgroups=24)),
+    ((512, 161, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=11)),
 ]
 
 
@@ -97,6 +115,9 @@ def test_routing_table_at_256_cus(key, expect):
         assert p[field] == value, (field, p)
     if p["kernel"] == "one_tile":
         assert p["lse_chunks"] == 1 and p["full_tiles"] == 0 and p["short_tokens"] == 0 and p["pair_rows"] == 0
+    elif p["kernel"] == "split_rows":
+        assert p["full_tiles"] == 0 and p["short_tokens"] == 0 and p["pair_rows"] == 0
+        assert p["workgroups"] == 12 * p["workgroups_per_head"]
     else:
         assert p["tile_tokens"] == 16 and p["rows_held"] == 0
         assert p["pair_rows"] == (4 if key[2] and key[0] <= 4 else 0)
@@ -145,12 +166,42 @@ def test_schedule_covers_every_token_once(cus):
         for n, lse in ((1, False), (1, True), (4, True), (6, True), (16, True), (100, True)):
             p = plan(n, int(S), lse, cus)
             assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["cus"] == cus
-            if p["kernel"] == "one_tile":
+            if p["kernel"] in ("one_tile", "split_rows"):
                 assert p["workgroups_per_head"] * p["tile_tokens"] >= S > (p["workgroups_per_head"] - 1) * p["tile_tokens"]
                 continue
             assert 0 <= p["short_tokens"] <= 16
             c = covered(p, int(S))
             assert np.all(c == 1), (n, S, cus, p)
+
+
+def test_split_rows_rule():
+    """Over n and S at several CU counts: the split-rows kernel exactly when
+    n > 16 with LSEs and 2 x 12 x ceil(S / 16) <= CUs; its tile holds each
+    wave to at most 32 rows (tile_tokens x n <= 256, one token at least), and
+    is the smallest such tile whose grid stays within one workgroup per CU,
+    else the largest; LSE chunks of 64 partials as the persistent kernel's
+    (1, 2, 4 or 8)."""
+    for cus in (256, 304, 80, 32):
+        for n in (1, 2, 16, 17, 31, 32, 33, 64, 65, 100, 128, 129, 256, 257, 512):
+            for S in (1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 100, 160, 161, 176, 250, 336):
+                for lse in (True, False):
+                    if not lse and n > 1:
+                        continue
+                    p = plan(n, S, lse, cus)
+                    want = lse and n > 16 and 24 * -(-S // 16) <= cus
+                    assert (p["kernel"] == "split_rows") == want, (n, S, cus, p)
+                    if not want:
+                        continue
+                    tt = p["tile_tokens"]
+                    cap = 4 if n <= 64 else 2 if n <= 128 else 1
+                    assert tt in (1, 2, 4) and tt <= cap
+                    assert p["lse_chunks"] == (1 if n <= 64 else 2 if n <= 128 else 4 if n <= 256 else 8)
+                    grid = lambda t: 12 * -(-S // t)
+                    if tt < cap:  # made smaller: the grid one size up also fits the CUs
+                        assert grid(2 * tt) <= cus
+                    if tt > 1:  # not smaller: the next smaller tile's grid would exceed the CUs
+                        assert grid(tt // 2) > cus, (n, S, cus, p)
+                    assert p["rows_held"] == min(16, 64 * p["lse_chunks"] * tt // 8)
 
 
 def test_grid_fits_a_dispatch():

@@ -84,6 +84,20 @@ def test_masks(gpu_lib):
     assert np.all(g["core"][33:] == 0) and np.all(g["lat"][33:] == 0)
 
 
+def test_split_rows_masks(gpu_lib):
+    """24 splits per request in the compact layout, with masks, on the
+    split-rows kernel (4-token tiles spanning two requests of q = 2, two waves
+    per token): kv_lens zeros count as -inf and tokens past the batch (120 of
+    128) are +0."""
+    m = gpu_lib
+    w = synth.request_major("rm_split_rows", per=24, q=2, S=128, seed=46, compact=True, kv_zero=0.3, batch_rows=120)
+    d = device_inputs(w)
+    p = m.plan(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], **d["layout"])
+    assert p["kernel"] == "split_rows" and p["tile_tokens"] == 4, p
+    g, ref, _ = check(m, w)
+    assert np.all(g["core"][120:] == 0) and np.all(g["lat"][120:] == 0)
+
+
 def test_shared_kv_row_dense_splits(gpu_lib):
     """Dense split partials with one shared row of KV lengths ([S // q]) and
     q = 4: a request with no KV yields +0 for its tokens."""
@@ -179,9 +193,10 @@ def test_large_request_major_sampled(gpu_lib):
         # 16 splits on 8-token tiles (the one-tile instance holding 16 rows)
         pytest.param(lambda: synth.request_major("rm_masked_n16", per=16, q=4, S=64, seed=46, compact=True,
                                                  kv_zero=0.3, batch_rows=50), id="n16_S64"),
-        # 20 splits: the persistent kernel with one tile per workgroup
-        pytest.param(lambda: synth.request_major("rm_masked_n20", per=20, q=4, S=64, seed=49, compact=True,
-                                                 kv_zero=0.3, batch_rows=50), id="n20_S64"),
+        # 20 splits: the persistent kernel with one tile per workgroup (with
+        # fewer tokens, 20 splits take the split-rows kernel)
+        pytest.param(lambda: synth.request_major("rm_masked_n20", per=20, q=4, S=400, seed=49, compact=True,
+                                                 kv_zero=0.3, batch_rows=350), id="n20_S400"),
         # several tiles per workgroup, the batch ending inside a tile
         pytest.param(lambda: synth.request_major("rm_masked_long", per=16, q=4, S=1104, seed=47, compact=True,
                                                  kv_zero=0.2, batch_rows=1001), id="n16_S1104"),
