@@ -948,6 +948,11 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
 // kernels' j = 0, 1, .., n - 1 (the merge admits any order; the float32
 // rounding stays within the same bound) and is fixed, so results repeat.
 constexpr int SPLIT_RB = 16;  // rows a wave holds at once
+constexpr int SPLIT_NB = 8;   // most batches of SPLIT_RB rows a wave streams
+
+// Batches of rows per wave of the instance for G waves per token and NCH LSE
+// chunks (n <= 64 NCH): 64 NCH / G rows.
+constexpr int split_batches(int g, int nch) { return 64 * nch / g <= SPLIT_RB ? 1 : 64 * nch / g / SPLIT_RB; }
 
 // Zero codes for tile slot tt, whose token does not exist (an MFMA column of
 // zeros, never stored).
@@ -959,7 +964,8 @@ __device__ __forceinline__ void empty_slot(const KArgs& a, int tt, int h, int la
 
 template <int G, int NCH>
 __global__ __launch_bounds__(THREADS) void mla_post_split_kernel(const KArgs a) {
-  static_assert(G == 2 || G == 4 || G == 8, "waves per token");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "waves per token");
+  static_assert(split_batches(G, NCH) <= SPLIT_NB, "rows per wave");
   constexpr int TT = WAVES / G;
   constexpr int RMAX = 64 * NCH / G;                    // most rows of one wave (n <= 64 NCH)
   constexpr int RB = RMAX < SPLIT_RB ? RMAX : SPLIT_RB;  // rows held at once
@@ -968,7 +974,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_split_kernel(const KArgs a) 
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
   __shared__ __attribute__((aligned(16))) uint8_t s_out[LDS_OUT];
-  __shared__ __attribute__((aligned(16))) float4 s_red[NRED][2][64];
+  __shared__ __attribute__((aligned(16))) float4 s_red[NRED > 0 ? NRED : 1][2][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1231,21 +1237,37 @@ int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
 // Tokens per workgroup of the split-rows kernel for a call with LSEs, or 0
 // when the call does not take it: more partials than the one-tile instance
 // holds, and at most half as many 16-token tiles as CUs (S <= 160 at 256
-// CUs). The tile is the largest (4, 2 or 1 tokens) whose waves hold at most
-// two batches of rows, made smaller while the grid stays within one
-// workgroup per CU. Measured at 256 CUs against the persistent kernel, 17 to
-// 512 splits: S = 16 10.8 -> 5.3 us (17 splits), 25.0 -> 5.9 (64), 171.6 ->
-// 21.9 (512); S = 160 13.1 -> 11.1 (17), 29.5 -> 22.7 (64), 212.8 -> 177.5
-// (512). At S = 192 the persistent kernel is 9-18% faster with 17 to 32
-// splits, within 2% from 33 to 96, 4-6% slower from 128; at S = 256 it is
-// faster by 3-23%.
+// CUs). The tile (8, 4, 2 or 1 tokens; at most SPLIT_NB batches of rows per
+// wave) is the one whose busiest CU finishes first by a simple model: a CU
+// runs ceil(grid / CUs) workgroups one after another, each costing a fixed
+// SPLIT_ROUND_ROWS plus its tile's token rows (TT n). On a tie, the larger
+// tile. Checked at 256 CUs against every tile forced in turn (17 to 512
+// splits, S = 16 to 160): the model's tile was the fastest, or within 2.5%
+// of it, at every point; the largest tile that fits one workgroup per CU
+// lost up to 16% (a grid just past the CU count: 200 and 256 splits at S = 96),
+// and tiles of at most 4 tokens and two batches up to 27%. Against the
+// persistent kernel: S = 16 10.8 -> 5.5 us (17 splits), 24.6 -> 6.0 (64),
+// 171.7 -> 21.2 (512); S = 160 13.1 -> 9.3 (17), 29.1 -> 19.8 (64), 208.6
+// -> 161.0 (512). Past S = 160 the persistent kernel is ahead (S = 176: 17
+// splits 13.0 against 14.2 us, 64 splits 29.5 against 31.6).
+constexpr int SPLIT_ROUND_ROWS = 150;
 int split_tile(int n, int S, int cus) {
   const int64_t ntiles = (S + TILE_T - 1) / TILE_T;
   if (n <= 2 * LAT_NMAX || 2 * NH * ntiles > cus) return 0;
-  int tt = 4;
-  while (tt > 1 && tt * n > 2 * WAVES * SPLIT_RB) tt /= 2;
-  while (tt > 1 && (int64_t)NH * ((S + tt / 2 - 1) / (tt / 2)) <= cus) tt /= 2;
-  return tt;
+  const int nch = lse_chunks(n);
+  int cap = WAVES;
+  while (cap > 1 && split_batches(WAVES / cap, nch) > SPLIT_NB) cap /= 2;
+  int best = cap;
+  int64_t best_cost = INT64_MAX;
+  for (int tt = cap; tt >= 1; tt /= 2) {
+    const int64_t grid = (int64_t)NH * ((S + tt - 1) / tt);
+    const int64_t cost = (grid + cus - 1) / cus * (SPLIT_ROUND_ROWS + (int64_t)tt * n);
+    if (cost < best_cost) {
+      best = tt;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // The launch for a validated call with S > 0 on a device of `cus` CUs: the
@@ -1288,8 +1310,8 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   if (stt > 0) {
     p.kernel = MLA_POST_KERNEL_SPLIT_ROWS;
     p.tile_tokens = stt;
-    p.lse_chunks = stt == 1 ? nch : n <= 64 ? 1 : 2;
-    p.rows_held = min(SPLIT_RB, 64 * p.lse_chunks * stt / WAVES);
+    p.lse_chunks = nch;
+    p.rows_held = min(SPLIT_RB, 64 * nch * stt / WAVES);
     p.workgroups_per_head = (S + stt - 1) / stt;
     p.workgroups = NH * p.workgroups_per_head;
     return p;
@@ -1326,27 +1348,36 @@ void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream)
   }
 }
 
+// Instances exist for the (tile, LSE chunks) pairs the plan can give; any
+// other pair is refused (the plan never makes one).
 template <int G, int NCH>
-void launch_split(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_post_split_kernel<G, NCH>), dim3((unsigned)p.workgroups), dim3(THREADS), 0, stream, k);
+int launch_split(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
+  if constexpr (split_batches(G, NCH) <= SPLIT_NB) {
+    hipLaunchKernelGGL((mla_post_split_kernel<G, NCH>), dim3((unsigned)p.workgroups), dim3(THREADS), 0, stream, k);
+    return launched(hipGetLastError());
+  } else {
+    return MLA_POST_EUNSUPPORTED;
+  }
+}
+
+template <int G>
+int launch_split_chunks(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
+  switch (p.lse_chunks) {
+    case 1: return launch_split<G, 1>(k, p, stream);
+    case 2: return launch_split<G, 2>(k, p, stream);
+    case 4: return launch_split<G, 4>(k, p, stream);
+    default: return launch_split<G, 8>(k, p, stream);
+  }
 }
 
 int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t stream) {
   if (p.kernel == MLA_POST_KERNEL_SPLIT_ROWS) {
-    const int c = p.lse_chunks;
-    if (p.tile_tokens == 4)
-      launch_split<2, 1>(k, p, stream);
-    else if (p.tile_tokens == 2)
-      c == 1 ? launch_split<4, 1>(k, p, stream) : launch_split<4, 2>(k, p, stream);
-    else if (c == 1)
-      launch_split<8, 1>(k, p, stream);
-    else if (c == 2)
-      launch_split<8, 2>(k, p, stream);
-    else if (c == 4)
-      launch_split<8, 4>(k, p, stream);
-    else
-      launch_split<8, 8>(k, p, stream);
-    return launched(hipGetLastError());
+    switch (p.tile_tokens) {
+      case 8: return launch_split_chunks<1>(k, p, stream);
+      case 4: return launch_split_chunks<2>(k, p, stream);
+      case 2: return launch_split_chunks<4>(k, p, stream);
+      default: return launch_split_chunks<8>(k, p, stream);
+    }
   }
   if (p.kernel == MLA_POST_KERNEL_ONE_TILE) {
     if (p.tile_tokens == TILE_T)

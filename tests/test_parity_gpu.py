@@ -199,9 +199,9 @@ def test_edge(gpu_lib, w):
 
 @pytest.mark.parametrize(
     "n,S",
-    [(6, 40), (16, 1100), (20, 400), (66, 340), (3, 1100), (4, 2100), (24, 150), (20, 40), (66, 20)],
+    [(6, 40), (16, 1100), (20, 400), (66, 340), (3, 1100), (4, 2100), (24, 150), (33, 64), (20, 40), (66, 20)],
     ids=["one_tile_instance", "persistent_n16", "persistent_n20", "persistent_two_chunks", "persistent_pair_n3",
-         "persistent_pair_n4", "split_rows_tile4", "split_rows_tile2", "split_rows_two_chunks"],
+         "persistent_pair_n4", "split_rows_tile8", "split_rows_tile4", "split_rows_tile2", "split_rows_two_chunks"],
 )
 def test_dead_rows_nan_inf_unused(gpu_lib, n, S):
     """Rows of weight 0 hold NaN and inf: the result equals the oracle's, which
@@ -220,27 +220,31 @@ def test_dead_rows_nan_inf_unused(gpu_lib, n, S):
     assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
 
 
-# (n, S, tokens per workgroup the plan gives at 256 CUs, workload options)
+# (n, S, tokens per workgroup the plan gives at 256 CUs, workload options):
+# every instance (waves per token G = 8 / tile, LSE chunks), ragged last tiles
 SPLIT_ROWS = [
-    # 2 waves per token (4-token tiles): rows j = g, g + 2, ..; a ragged last
-    # tile; with more than 32 splits a second batch of rows per wave
-    (20, 157, 4, dict(p_neg_inf=0.2)),
-    (32, 99, 4, dict(p_neg_inf=0.3, p_nan=0.05)),
+    # one wave per token (8-token tiles): a wave streams all of a token's rows,
+    # up to 4 batches of 16 (one LSE chunk) or 8 (two)
+    (20, 157, 8, dict(p_neg_inf=0.2)),
+    (100, 130, 8, dict(p_neg_inf=0.1)),
+    # 2 waves per token (4-token tiles): rows j = g, g + 2, ..; 1, 2, 4 chunks
     (33, 64, 4, dict(p_neg_inf=0.1)),
     (64, 43, 4, dict(p_neg_inf=0.05, p_pos_inf=0.05)),
-    # 4 waves per token (2-token tiles): n not a multiple of 4; 2 LSE chunks
-    # and two batches of rows per wave
+    (100, 61, 4, dict(p_neg_inf=0.2)),
+    (200, 50, 4, dict(p_neg_inf=0.3, p_nan=0.05)),
+    # 4 waves per token (2-token tiles): n not a multiple of 4; 1, 2, 4, 8 chunks
     (40, 33, 2, dict(p_neg_inf=0.1)),
-    (100, 61, 2, dict(p_neg_inf=0.2)),
-    # 8 waves per token, one token per workgroup: 1, 2, 4 and 8 LSE chunks;
-    # with 129 and more splits a wave streams further batches of rows
+    (128, 41, 2, dict(p_neg_inf=0.1)),
+    (250, 35, 2, dict(p_neg_inf=0.2)),
+    (300, 41, 2, dict(p_neg_inf=0.4)),
+    # 8 waves per token, one token per workgroup: 1, 2, 4 and 8 chunks
     (50, 10, 1, dict(p_neg_inf=0.2)),
     (100, 7, 1, dict(p_neg_inf=0.1)),
     (129, 3, 1, dict(p_neg_inf=0.1)),
     (300, 2, 1, dict(p_neg_inf=0.4, p_nan=0.05)),
     (512, 1, 1, dict(p_neg_inf=0.02)),
     # tokens all of whose partials are dead: exact zeros
-    (24, 150, 4, dict(p_neg_inf=0.9)),
+    (24, 150, 8, dict(p_neg_inf=0.9)),
 ]
 
 

@@ -42,7 +42,7 @@ def plan(n, S, lse=True, cus=256):
 # and the instance holds every row (8-token tiles up to 3 workgroups per CU,
 # i.e. S <= 512, with up to 16 rows; 16-token tiles with up to 8 rows; the
 # fewest of 2, 4, 8, 16 rows that hold n); the split-rows kernel for more
-# than 16 partials with LSEs up to S = 160 (4-, 2- or 1-token tiles); else
+# than 16 partials with LSEs up to S = 160 (8-, 4-, 2- or 1-token tiles); else
 # the persistent kernel with 64 workgroups per head, 40 from 65 to 96 tiles,
 # and leftover tokens dealt out evenly from n = 6 (whole 16-token tiles
 # below).
@@ -88,18 +88,20 @@ TABLE = [
     ((65, 400, True), dict(kernel="persistent", lse_chunks=2)),
     ((200, 400, True), dict(kernel="persistent", lse_chunks=4)),
     ((512, 400, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=25)),
-    # the split-rows kernel: the largest tile whose waves hold at most two
-    # batches of 16 rows (4 tokens up to 64 splits, 2 up to 128, else 1),
-    # smaller while the grid stays within one workgroup per CU
+    # the split-rows kernel: the tile (8, 4, 2 or 1 tokens, at most 8 batches
+    # of 16 rows per wave) whose busiest CU has the least to do by the round
+    # model; one round: the largest grid within the CUs
     ((17, 64, True), dict(kernel="split_rows", tile_tokens=4, rows_held=16, lse_chunks=1, workgroups_per_head=16,
                           workgroups=192)),
     ((17, 16, True), dict(kernel="split_rows", tile_tokens=1, rows_held=8, workgroups_per_head=16)),
     ((17, 32, True), dict(kernel="split_rows", tile_tokens=2, rows_held=16, workgroups_per_head=16)),
-    ((64, 160, True), dict(kernel="split_rows", tile_tokens=4, lse_chunks=1, workgroups_per_head=40, workgroups=480)),
-    ((64, 100, True), dict(kernel="split_rows", tile_tokens=4, lse_chunks=1)),
-    ((65, 100, True), dict(kernel="split_rows", tile_tokens=2, rows_held=16, lse_chunks=2, workgroups_per_head=50)),
+    ((64, 160, True), dict(kernel="split_rows", tile_tokens=8, lse_chunks=1, workgroups_per_head=20, workgroups=240)),
+    ((64, 100, True), dict(kernel="split_rows", tile_tokens=8, lse_chunks=1, workgroups_per_head=13)),
+    ((65, 100, True), dict(kernel="split_rows", tile_tokens=8, rows_held=16, lse_chunks=2, workgroups_per_head=13)),
     ((128, 7, True), dict(kernel="split_rows", tile_tokens=1, lse_chunks=2, workgroups_per_head=7, workgroups=84)),
-    ((129, 100, True), dict(kernel="split_rows", tile_tokens=1, rows_held=16, lse_chunks=4)),
+    # 129 splits at S = 100: 4-token tiles (the most 4 LSE chunks allow) would
+    # put 2 workgroups on some CUs; 2-token tiles, 3 rounds of half the rows, win
+    ((129, 100, True), dict(kernel="split_rows", tile_tokens=2, rows_held=16, lse_chunks=4, workgroups=600)),
     ((200, 5, True), dict(kernel="split_rows", tile_tokens=1, lse_chunks=4)),
     ((512, 2, True), dict(kernel="split_rows", tile_tokens=1, rows_held=16, lse_chunks=8, workgroups_per_head=2,
                           workgroups=24)),
@@ -174,16 +176,31 @@ def test_schedule_covers_every_token_once(cus):
             assert np.all(c == 1), (n, S, cus, p)
 
 
+def split_model(n, S, cus):
+    """The tile the documented model picks: tiles of 8, 4, 2, 1 tokens whose
+    waves (8 / tile per token) stream at most 8 batches of 16 rows of an
+    instance with ceil(n / 64) rounded to 1, 2, 4, 8 LSE chunks; cost =
+    ceil(grid / CUs) x (150 + tile x n); the least cost, the larger tile on a
+    tie."""
+    nch = 1 if n <= 64 else 2 if n <= 128 else 4 if n <= 256 else 8
+    best, best_cost = None, None
+    for tt in (8, 4, 2, 1):
+        g = 8 // tt
+        if 64 * nch // g > 16 * 8:
+            continue
+        cost = -(-12 * -(-S // tt) // cus) * (150 + tt * n)
+        if best_cost is None or cost < best_cost:
+            best, best_cost = tt, cost
+    return best, nch
+
+
 def test_split_rows_rule():
     """Over n and S at several CU counts: the split-rows kernel exactly when
-    n > 16 with LSEs and 2 x 12 x ceil(S / 16) <= CUs; its tile holds each
-    wave to at most 32 rows (tile_tokens x n <= 256, one token at least), and
-    is the smallest such tile whose grid stays within one workgroup per CU,
-    else the largest; LSE chunks of 64 partials as the persistent kernel's
-    (1, 2, 4 or 8)."""
+    n > 16 with LSEs and 2 x 12 x ceil(S / 16) <= CUs, with the tile and LSE
+    chunks of the model and the rows a wave holds at once."""
     for cus in (256, 304, 80, 32):
         for n in (1, 2, 16, 17, 31, 32, 33, 64, 65, 100, 128, 129, 256, 257, 512):
-            for S in (1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 100, 160, 161, 176, 250, 336):
+            for S in (1, 2, 3, 5, 16, 22, 31, 32, 33, 43, 63, 64, 86, 100, 144, 160, 161, 176, 250, 336):
                 for lse in (True, False):
                     if not lse and n > 1:
                         continue
@@ -192,16 +209,10 @@ def test_split_rows_rule():
                     assert (p["kernel"] == "split_rows") == want, (n, S, cus, p)
                     if not want:
                         continue
-                    tt = p["tile_tokens"]
-                    cap = 4 if n <= 64 else 2 if n <= 128 else 1
-                    assert tt in (1, 2, 4) and tt <= cap
-                    assert p["lse_chunks"] == (1 if n <= 64 else 2 if n <= 128 else 4 if n <= 256 else 8)
-                    grid = lambda t: 12 * -(-S // t)
-                    if tt < cap:  # made smaller: the grid one size up also fits the CUs
-                        assert grid(2 * tt) <= cus
-                    if tt > 1:  # not smaller: the next smaller tile's grid would exceed the CUs
-                        assert grid(tt // 2) > cus, (n, S, cus, p)
-                    assert p["rows_held"] == min(16, 64 * p["lse_chunks"] * tt // 8)
+                    tt, nch = split_model(n, S, cus)
+                    assert (p["tile_tokens"], p["lse_chunks"]) == (tt, nch), (n, S, cus, p)
+                    assert p["rows_held"] == min(16, 64 * nch * tt // 8)
+                    assert p["workgroups"] == 12 * -(-S // tt)
 
 
 def test_grid_fits_a_dispatch():

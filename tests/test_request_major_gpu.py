@@ -84,18 +84,20 @@ def test_masks(gpu_lib):
     assert np.all(g["core"][33:] == 0) and np.all(g["lat"][33:] == 0)
 
 
-def test_split_rows_masks(gpu_lib):
-    """24 splits per request in the compact layout, with masks, on the
-    split-rows kernel (4-token tiles spanning two requests of q = 2, two waves
-    per token): kv_lens zeros count as -inf and tokens past the batch (120 of
-    128) are +0."""
+@pytest.mark.parametrize("per,q,S,end,tt", [(24, 2, 128, 120, 8), (40, 4, 40, 34, 2)], ids=["tile8", "tile2"])
+def test_split_rows_masks(gpu_lib, per, q, S, end, tt):
+    """Many splits per request in the compact layout, with masks, on the
+    split-rows kernel: 8-token tiles spanning four requests of q = 2 (one wave
+    per token), and 2-token tiles inside requests of q = 4 (four waves per
+    token). kv_lens zeros count as -inf and tokens past the batch are +0."""
     m = gpu_lib
-    w = synth.request_major("rm_split_rows", per=24, q=2, S=128, seed=46, compact=True, kv_zero=0.3, batch_rows=120)
+    w = synth.request_major(f"rm_split_rows_{tt}", per=per, q=q, S=S, seed=46 + tt, compact=True, kv_zero=0.3,
+                            batch_rows=end)
     d = device_inputs(w)
     p = m.plan(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], **d["layout"])
-    assert p["kernel"] == "split_rows" and p["tile_tokens"] == 4, p
+    assert p["kernel"] == "split_rows" and p["tile_tokens"] == tt, p
     g, ref, _ = check(m, w)
-    assert np.all(g["core"][120:] == 0) and np.all(g["lat"][120:] == 0)
+    assert np.all(g["core"][end:] == 0) and np.all(g["lat"][end:] == 0)
 
 
 def test_shared_kv_row_dense_splits(gpu_lib):
