@@ -1246,10 +1246,12 @@ int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
 // of it, at every point; the largest tile that fits one workgroup per CU
 // lost up to 16% (a grid just past the CU count: 200 and 256 splits at S = 96),
 // and tiles of at most 4 tokens and two batches up to 27%. Against the
-// persistent kernel: S = 16 10.8 -> 5.5 us (17 splits), 24.6 -> 6.0 (64),
-// 171.7 -> 21.2 (512); S = 160 13.1 -> 9.3 (17), 29.1 -> 19.8 (64), 208.6
-// -> 161.0 (512). Past S = 160 the persistent kernel is ahead (S = 176: 17
-// splits 13.0 against 14.2 us, 64 splits 29.5 against 31.6).
+// persistent kernel: S = 16 10.8 -> 5.5 us (17 splits), 24.7 -> 6.1 (64),
+// 171.0 -> 21.8 (512); S = 160 13.1 -> 9.4 (17), 29.4 -> 20.0 (64), 212.4
+// -> 163.3 (512). Past S = 160 the persistent kernel is 5-11% ahead with up
+// to 32 splits (S = 176: 13.1 against 14.4 us with 17); with 64 to 512 the
+// split-rows kernel stays 2-11% ahead up to S = 192 and within 2% either
+// way at S = 256, so one bound serves all.
 constexpr int SPLIT_ROUND_ROWS = 150;
 int split_tile(int n, int S, int cus) {
   const int64_t ntiles = (S + TILE_T - 1) / TILE_T;
