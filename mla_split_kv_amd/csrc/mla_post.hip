@@ -1194,21 +1194,46 @@ int device_cus() {
   return cus;
 }
 
-// Workgroups per head (the grid is 12 times that): one per token tile while
-// that is at most `fill` (WG_PER_CU workgroups per CU in the grid, 2 of them
-// resident: 64 at 256 CUs); up to 1.5 fill tiles, the most that are all
-// resident at once (2 per CU, a multiple of 8 so that the 12 heads of a slot
-// share an XCD: 40), so that every workgroup runs about two tiles back to
-// back in one round instead of a full and a short tile in 1.5 rounds;
-// beyond that, fill. Measured at 65 to 96 tiles (S = 1040 to 1536) with 4 to
-// 24 splits, 40 against 64: 16 splits S = 1100 43.5 -> 36.7 us, S = 1280
-// 45.4 -> 40.3 us, within 2% either way at S = 1536, and 64 ahead again from
-// about 100 tiles.
-int workgroups_per_head(int S, int cus) {
+// Workgroups per head of the persistent kernel (the grid is 12 times that).
+// `fill` is WG_PER_CU workgroups per CU in the grid, 2 of them resident (64
+// at 256 CUs); `one_round` the most that are all resident at once (2 per CU,
+// a multiple of 8 so that the 12 heads of a slot share an XCD: 40).
+// - At most one workgroup per CU with one tile each: one per tile.
+// - Up to one_round tiles: one_round, each workgroup one short tile of S /
+//   one_round tokens, all resident and every CU with at most 2 (one tile
+//   per workgroup would put 2 full tiles on the CUs past the first round).
+//   Except with at most 128 splits when only the last tile is past the first
+//   round and one tile per workgroup leaves fewer tokens on the busiest CU
+//   (its 16 and the last tile's, against 2 short tiles). With more splits 2
+//   workgroups per CU stream faster than one alone, and one_round stays.
+// - Up to 2 workgroups per CU with one tile each: one per tile.
+// - Up to fill tiles: fill, every CU running 3 workgroups of S / fill tokens
+//   (one tile each would leave some CUs 3 full tiles, others 2).
+// - Up to 1.5 fill tiles: one_round, so that every workgroup runs about two
+//   tiles back to back in one round instead of a full and a short tile in 1.5
+//   rounds. Measured at 65 to 96 tiles (S = 1040 to 1536) with 4 to 24
+//   splits, 40 against 64: 16 splits S = 1100 43.5 -> 36.7 us, S = 1280 45.4
+//   -> 40.3 us, within 2% either way at S = 1536, and 64 ahead again from
+//   about 100 tiles.
+// - Beyond that, fill.
+// Measured at 256 CUs, 16 to 256 splits, S = 337 to 960, against one tile
+// per workgroup up to fill tiles (the rule before) and against 40 and 64
+// workgroups per head throughout: within 1.5% of the fastest of the three at
+// every point, and up to 26% faster than before (64 splits: S = 352 66.2 ->
+// 49.7 us, S = 704 101.9 -> 87.7 us; 16 splits, S = 768: 30.3 -> 28.2 us).
+int workgroups_per_head(int S, int n, int cus) {
   const int ntiles = (S + TILE_T - 1) / TILE_T;
   const int fill = max(1, cus * WG_PER_CU / NH);
-  if (ntiles <= fill) return ntiles;
   const int one_round = (2 * cus / NH) / XCDS * XCDS;
+  if ((int64_t)NH * ntiles <= cus) return ntiles;
+  if (one_round > 0 && ntiles <= one_round) {
+    const int last = S - (ntiles - 1) * TILE_T;
+    const int short_tile = (S + one_round - 1) / one_round;
+    if (n <= 128 && (int64_t)NH * (ntiles - 1) < cus && TILE_T + last < 2 * short_tile) return ntiles;
+    return one_round;
+  }
+  if ((int64_t)NH * ntiles <= 2 * (int64_t)cus) return min(ntiles, fill);
+  if (ntiles <= fill) return fill;
   if (2 * ntiles <= 3 * fill && one_round > 0) return one_round;
   return fill;
 }
@@ -1284,7 +1309,7 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   const int S = a->S, n = a->n;
   const int nch = nolse ? 1 : lse_chunks(n);
   const int ntiles = (S + TILE_T - 1) / TILE_T;
-  const int wph = workgroups_per_head(S, cus);
+  const int wph = workgroups_per_head(S, n, cus);
   // One or two partials with LSEs take the one-tile instance at every size:
   // a 16-token tile then holds 2 rows per token (59 registers, 4 workgroups
   // per CU), and the device refills CUs with new workgroups as others end.
@@ -1293,7 +1318,7 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   // 8192; with 3 or 4 splits, or without LSEs, it was slower beyond S = 1024.
   // Up to S = 2^20: a dispatch counts its work-items in 32 bits, and 12
   // workgroups of 512 per 16 tokens would overflow that past S = 11M.
-  const bool fits = wph == ntiles && nch == 1;
+  const bool fits = ntiles <= max(1, cus * WG_PER_CU / NH) && nch == 1;
   if (fits || (!nolse && n <= 2 && S <= ONE_TILE_SMAX)) {
     const int tt = fits ? latency_tile(S, cus) : TILE_T;
     if (nolse || n <= lat_nmax(tt)) {

@@ -177,7 +177,14 @@ def test_persistent_multi_tile_sampled(gpu_lib, make):
         pytest.param(lambda: synth.dense_splits("latency16_n2", 2, 777, seed=37, p_neg_inf=0.3), id="latency16_n2"),
         pytest.param(lambda: synth.dense_splits("latency8_n4", 4, 300, seed=38, p_neg_inf=0.3, p_nan=0.05),
                      id="latency8_n4"),
-        pytest.param(lambda: synth.dense_splits("n16_S800", 16, 800, seed=34, p_neg_inf=0.2), id="n16_persistent_one_tile_each"),
+        # between one workgroup per CU and 64 tiles per head: every workgroup
+        # one short tile (64 per head, two of them with none at S = 800; 40
+        # per head, one with none, at S = 345), one full tile each (42 tiles),
+        # and one per tile with only the 1-token last tile past the first round
+        pytest.param(lambda: synth.dense_splits("n16_S800", 16, 800, seed=34, p_neg_inf=0.2), id="n16_persistent_short_tiles"),
+        pytest.param(lambda: synth.dense_splits("n20_S345", 20, 345, seed=40, p_neg_inf=0.2), id="n20_persistent_40_short"),
+        pytest.param(lambda: synth.dense_splits("n24_S672", 24, 672, seed=41, p_neg_inf=0.2), id="n24_persistent_42_full"),
+        pytest.param(lambda: synth.dense_splits("n40_S337", 40, 337, seed=42, p_neg_inf=0.2), id="n40_persistent_22_tiles"),
         # S past one device-filling wave of workgroups (more than 64 tiles per
         # head at 256 CUs): the persistent kernel, with a ragged last tile
         pytest.param(lambda: synth.dense_splits("persistent_ragged", 3, 1030, seed=23, p_neg_inf=0.2), id="persistent_ragged"),

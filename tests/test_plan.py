@@ -43,7 +43,8 @@ def plan(n, S, lse=True, cus=256):
 # i.e. S <= 512, with up to 16 rows; 16-token tiles with up to 8 rows; the
 # fewest of 2, 4, 8, 16 rows that hold n); the split-rows kernel for more
 # than 16 partials with LSEs up to S = 160 (8-, 4-, 2- or 1-token tiles); else
-# the persistent kernel with 64 workgroups per head, 40 from 65 to 96 tiles,
+# the persistent kernel with 64 workgroups per head (40 up to 40 tiles and
+# from 65 to 96 tiles, one per tile where that keeps at most 1 or 2 per CU),
 # and leftover tokens dealt out evenly from n = 6 (whole 16-token tiles
 # below).
 TABLE = [
@@ -63,7 +64,7 @@ TABLE = [
     ((5, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8)),
     ((9, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16)),
     ((1, 1000, False), dict(kernel="one_tile", tile_tokens=16, rows_held=1, workgroups_per_head=63)),
-    ((16, 513, True), dict(kernel="persistent", workgroups_per_head=33, full_tiles=0, short_tokens=16)),
+    ((16, 513, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=0, short_tokens=13)),
     ((17, 161, True), dict(kernel="persistent", workgroups_per_head=11, full_tiles=0, short_tokens=15)),
     ((1, 1025, False), dict(kernel="persistent", workgroups_per_head=40, pair_rows=0)),
     # both tokens' rows a tile ahead for n <= 4 with LSEs
@@ -87,7 +88,20 @@ TABLE = [
     ((64, 400, True), dict(kernel="persistent", lse_chunks=1)),
     ((65, 400, True), dict(kernel="persistent", lse_chunks=2)),
     ((200, 400, True), dict(kernel="persistent", lse_chunks=4)),
-    ((512, 400, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=25)),
+    ((512, 400, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=40)),
+    # between one workgroup per CU and fill tiles: 40 per head up to 40 tiles
+    # (one short tile each), one per tile while that is at most 2 per CU (41,
+    # 42 tiles), else 64 (a short tile each); one tile each at S = 337 with
+    # up to 128 splits (only the 1-token last tile is past the first round)
+    ((20, 337, True), dict(kernel="persistent", workgroups_per_head=22, full_tiles=0, short_tokens=16)),
+    ((256, 337, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=0, short_tokens=9)),
+    ((20, 352, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=0, short_tokens=9)),
+    ((32, 640, True), dict(kernel="persistent", workgroups_per_head=40, full_tiles=1, short_tokens=0)),
+    ((32, 656, True), dict(kernel="persistent", workgroups_per_head=41, full_tiles=1, short_tokens=0)),
+    ((32, 672, True), dict(kernel="persistent", workgroups_per_head=42, full_tiles=1, short_tokens=0)),
+    ((32, 688, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=0, short_tokens=11)),
+    ((16, 768, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=0, short_tokens=12)),
+    ((64, 1024, True), dict(kernel="persistent", workgroups_per_head=64, full_tiles=1, short_tokens=0)),
     # the split-rows kernel: the tile (8, 4, 2 or 1 tokens, at most 8 batches
     # of 16 rows per wave) whose busiest CU has the least to do by the round
     # model; one round: the largest grid within the CUs
@@ -162,10 +176,11 @@ def test_schedule_covers_every_token_once(cus):
     short tiles hold at most 16 tokens, and the grid is 12 per head; the
     one-tile instance's grid covers S."""
     rng = np.random.default_rng(cus)
-    sizes = sorted(set([1, 2, 15, 16, 17, 500, 1023, 1024, 1025, 1100, 1536, 1537, 2064, 4096, 4112, 9000]
+    sizes = sorted(set([1, 2, 15, 16, 17, 337, 352, 500, 640, 656, 672, 688, 768, 960, 1023, 1024, 1025, 1100, 1536,
+                        1537, 2064, 4096, 4112, 9000]
                        + list(rng.integers(1, 20000, size=60))))
     for S in sizes:
-        for n, lse in ((1, False), (1, True), (4, True), (6, True), (16, True), (100, True)):
+        for n, lse in ((1, False), (1, True), (4, True), (6, True), (16, True), (20, True), (100, True), (256, True)):
             p = plan(n, int(S), lse, cus)
             assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["cus"] == cus
             if p["kernel"] in ("one_tile", "split_rows"):
