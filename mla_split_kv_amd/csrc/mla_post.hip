@@ -379,15 +379,35 @@ __device__ __forceinline__ const uint8_t* row_base(const KArgs& a, int t, int h)
   return a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (int64_t)(t / a.q) * a.o_sr;
 }
 
-// One partial and no LSE: token t's row (tile slot tt, already loaded: v)
-// is the attention output itself, used as the bf16 latents unless its
-// request is masked as having no KV or the token lies past the batch
-// (`empty`); -> MXFP4 into LDS.
+// The LSE of token t's one partial (n = 1), or 0 without LSEs; t is clamped
+// to S - 1, so the load is valid for tokens a tile does not own.
+__device__ __forceinline__ float lse_one(const KArgs& a, int t, int h) {
+  if (!a.lse) return 0.f;
+  const int tc = min(t, a.S - 1);
+  return a.lse[(int64_t)(tc / a.q) * a.l_sr + (int64_t)tc * a.l_st + (int64_t)h * a.l_sh];
+}
+
+// One partial: token t's row (tile slot tt, already loaded: v) is its
+// latents, unless its request is masked as having no KV, the token lies
+// past the batch (`empty`) or, with an LSE, that LSE sanitises to -inf.
+// With an LSE this is the merge of one partial exactly: its weight is
+// exp(0) / 1 = 1 or 0, and 1 * x + 0 is x except that -0 becomes +0 (the
+// merge's sum starts at +0), so -0 elements are made +0 here. -> MXFP4 into
+// LDS.
 __device__ __forceinline__ void copy_stage(const KArgs& a, int t, int tt, int h, int lane, bool live, bool empty,
-                                           const uint4& v, uint8_t* s_codes, uint8_t* s_scales) {
+                                           const uint4& v, float lse, uint8_t* s_codes, uint8_t* s_scales) {
   uint32_t lat[4] = {0u, 0u, 0u, 0u};
-  if (live && !empty && !(a.kv_lens && a.kv_lens[t / a.q] == 0)) {
+  const bool dead = a.lse != nullptr && sane(lse) == -INFINITY;
+  if (live && !empty && !dead && !(a.kv_lens && a.kv_lens[t / a.q] == 0)) {
     lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
+    if (a.lse) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (lat[k] & 0x7FFFu) ? (lat[k] & 0xFFFFu) : 0u;
+        const uint32_t hi = (lat[k] & 0x7FFF0000u) ? (lat[k] & 0xFFFF0000u) : 0u;
+        lat[k] = hi | lo;
+      }
+    }
   }
   quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
 }
@@ -632,11 +652,12 @@ __device__ __forceinline__ void head_and_slot(int& h, int& slot) {
   }
 }
 
-// PAIR: rows of each of a wave's two tokens issued a tile ahead (instantiated
-// with 4, for n <= 4; 0: the first PF_ROWS rows of the first token only).
-template <bool NOLSE, int NCH, int PAIR>
+// COPY: one partial, copied (copy_stage) rather than merged. PAIR: rows of
+// each of a wave's two tokens issued a tile ahead (instantiated with 4, for
+// 2 <= n <= 4; 0: the first PF_ROWS rows of the first token only).
+template <bool COPY, int NCH, int PAIR>
 __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg_per_head) {
-  static_assert(PAIR == 0 || (NCH == 1 && !NOLSE), "both tokens' rows ahead only for n <= 64 with LSEs");
+  static_assert(PAIR == 0 || (NCH == 1 && !COPY), "both tokens' rows ahead only for merged partials, n <= 64");
   constexpr int NPF = PAIR ? 2 * PAIR : PF_ROWS;  // rows in flight across the barrier
   constexpr int NPRE_A = PAIR ? PAIR : PF_ROWS, NPRE_B = PAIR;
   // two LDS buffers: a wave may merge tile i+1 while others still read tile i
@@ -651,7 +672,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int h, slot;  // this workgroup's head, fixed, and its slot of the head's tiles
   head_and_slot(h, slot);
-  const TileSched ts = tile_sched(a.S, wg_per_head, slot, spread_leftover(NOLSE, a.n));
+  const TileSched ts = tile_sched(a.S, wg_per_head, slot, spread_leftover(COPY, a.n));
   const int tl = lane & 15;  // MFMA row / column index of this lane
   const int kb = lane >> 4;  // MFMA K block of this lane
 
@@ -680,8 +701,11 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
   int t0, tend, n0, nend;
   tile_span(ts, 0, t0, tend);
   tile_span(ts, 1, n0, nend);
-  if constexpr (NOLSE) {
-    // without LSEs a token's one row is issued a tile ahead, both tokens'
+  float pl[TOK_PER_WAVE] = {0.f, 0.f};  // one partial: the LSEs (if any) of the rows in flight
+  if constexpr (COPY) {
+    // one partial: a token's one row (and LSE) is issued a tile ahead, both tokens'
+    pl[0] = lse_one(a, t0 + wave * TOK_PER_WAVE, h);
+    pl[1] = lse_one(a, t0 + wave * TOK_PER_WAVE + 1, h);
     issue_rows_early<1>(a, t0 + wave * TOK_PER_WAVE, tend, batch_end, h, lane, pv);
     issue_rows_early<1>(a, t0 + wave * TOK_PER_WAVE + 1, tend, batch_end, h, lane, pv + 1);
   } else {
@@ -709,9 +733,11 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
     // S re-reads row S - 1 (a token the tile does not own is never stored)
     const int t_out = min(t0 + tl, a.S - 1);
     const uint2 g4 = load_nt8(a.gate + ((int64_t)t_out * GROWS + h * VD + wave * 16 + kb * 4) * 2);
-    if constexpr (NOLSE) {
-      copy_stage(a, tA, ttA, h, lane, liveA, emptyA, pv[0], codes, scales);
-      copy_stage(a, tB, ttB, h, lane, liveB, emptyB, pv[1], codes, scales);
+    if constexpr (COPY) {
+      copy_stage(a, tA, ttA, h, lane, liveA, emptyA, pv[0], pl[0], codes, scales);
+      copy_stage(a, tB, ttB, h, lane, liveB, emptyB, pv[1], pl[1], codes, scales);
+      pl[0] = lse_one(a, n0 + wave * TOK_PER_WAVE, h);
+      pl[1] = lse_one(a, n0 + wave * TOK_PER_WAVE + 1, h);
       issue_rows_early<1>(a, n0 + wave * TOK_PER_WAVE, nend, batch_end, h, lane, pv);
       issue_rows_early<1>(a, n0 + wave * TOK_PER_WAVE + 1, nend, batch_end, h, lane, pv + 1);
     } else {
@@ -720,7 +746,7 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
       merge_stage<NCH, NPRE_B, PAIR == 0>(a, tB, ttB, h, lane, liveB, emptyB, wB, pv + NPRE_A, pw + NPRE_A, codes,
                                            scales);
     }
-    if constexpr (!NOLSE) {
+    if constexpr (!COPY) {
       tile_weights<NCH>(a, n0, nend, batch_end, wave, lane, lA, kA, lB, kB, wA, wB);
       prefetch_lse<NCH>(a, m0, h, wave, lane, lA, kA, lB, kB);
       issue_next_rows<NCH, PAIR>(a, n0, h, wave, lane, wA, wB, pv, pw);
@@ -839,8 +865,9 @@ constexpr int lat_nmax(int tt) { return tt <= WAVES ? 2 * LAT_NMAX : LAT_NMAX; }
 // small batch spreads over more CUs. Wave w owns token slots w and w + 8;
 // slots at or past TT are empty (zero codes, nothing loaded, nothing stored),
 // so MFMA columns of those slots carry zeros.
-// NM: rows per token held at once (the instance for n <= NM).
-template <bool NOLSE, int TT, int NM>
+// NM: rows per token held at once (the instance for n <= NM). COPY: one
+// partial, copied (copy_stage) rather than merged.
+template <bool COPY, int TT, int NM>
 __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
@@ -868,15 +895,14 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
   const bool liveA = ttA < TT && tA < a.S, liveB = ttB < TT && tB < a.S;
   const bool useA = liveA && tA < batch_end, useB = liveB && tB < batch_end;
   uint32_t latA[4] = {0u, 0u, 0u, 0u}, latB[4] = {0u, 0u, 0u, 0u};
-  if constexpr (NOLSE) {
-    if (useA && !(a.kv_lens && a.kv_lens[tA / a.q] == 0)) {
-      const uint4 v = load_row16(row_base(a, tA, h), lane);
-      latA[0] = v.x; latA[1] = v.y; latA[2] = v.z; latA[3] = v.w;
-    }
-    if (useB && !(a.kv_lens && a.kv_lens[tB / a.q] == 0)) {
-      const uint4 v = load_row16(row_base(a, tB, h), lane);
-      latB[0] = v.x; latB[1] = v.y; latB[2] = v.z; latB[3] = v.w;
-    }
+  if constexpr (COPY) {
+    // one partial: its row, kept as copy_stage keeps it
+    const float lsA = lse_one(a, tA, h), lsB = lse_one(a, tB, h);
+    uint4 vA = make_uint4(0u, 0u, 0u, 0u), vB = make_uint4(0u, 0u, 0u, 0u);
+    if (useA) vA = load_row16(row_base(a, tA, h), lane);
+    if (useB) vB = load_row16(row_base(a, tB, h), lane);
+    copy_stage(a, tA, ttA, h, lane, liveA, !useA, vA, lsA, s_codes, s_scales);
+    copy_stage(a, tB, ttB, h, lane, liveB, !useB, vB, lsB, s_codes, s_scales);
   } else {
     // LSE loads first, then every row, and only then anything that waits
     float lA[1] = {-INFINITY}, lB[1] = {-INFINITY};
@@ -925,9 +951,9 @@ __global__ __launch_bounds__(THREADS) void mla_post_latency_kernel(const KArgs a
 #pragma unroll
       for (int k = 0; k < 4; ++k) latB[k] = pack_bf16(accB[2 * k], accB[2 * k + 1]);
     }
+    quant_to_lds(a, tA, ttA, h, lane, liveA, latA, s_codes, s_scales);
+    quant_to_lds(a, tB, ttB, h, lane, liveB, latB, s_codes, s_scales);
   }
-  quant_to_lds(a, tA, ttA, h, lane, liveA, latA, s_codes, s_scales);
-  quant_to_lds(a, tB, ttB, h, lane, liveB, latB, s_codes, s_scales);
   __syncthreads();
   tile_wuv_store(a, wave, tl, kb, wv, sa, s_codes, s_scales, s_out, out);
 }
@@ -1299,41 +1325,47 @@ int split_tile(int n, int S, int cus) {
 
 // The launch for a validated call with S > 0 on a device of `cus` CUs: the
 // one-tile instance when one token tile per workgroup fills the device at
-// most once and the instance can hold every row of a token, or when n <= 2
-// with LSEs; else the persistent kernel. mla_post launches exactly this.
+// most once and the instance can hold every row of a token, or when n == 2
+// with LSEs; the split-rows kernel for many partials and few tokens; else
+// the persistent kernel. One partial is copied. mla_post launches exactly
+// this.
 mla_post_plan make_plan(const mla_post_args* a, int cus) {
   mla_post_plan p;
   memset(&p, 0, sizeof(p));
   p.cus = cus;
-  const bool nolse = a->lse == nullptr;
+  // one partial (with or without an LSE) is copied rather than merged
+  const bool copy = a->n == 1;
   const int S = a->S, n = a->n;
-  const int nch = nolse ? 1 : lse_chunks(n);
+  const int nch = lse_chunks(n);
   const int ntiles = (S + TILE_T - 1) / TILE_T;
   const int wph = workgroups_per_head(S, n, cus);
-  // One or two partials with LSEs take the one-tile instance at every size:
-  // a 16-token tile then holds 2 rows per token (59 registers, 4 workgroups
+  // Two partials with LSEs take the one-tile instance at every size: a
+  // 16-token tile then holds 2 rows per token (59 registers, 4 workgroups
   // per CU), and the device refills CUs with new workgroups as others end.
-  // Measured against the persistent kernel: one split S = 2048 19.0 -> 15.5
-  // us, 4096 29.4 -> 26.7 us; two splits 2048 19.9 -> 16.9 us, equal at
-  // 8192; with 3 or 4 splits, or without LSEs, it was slower beyond S = 1024.
-  // Up to S = 2^20: a dispatch counts its work-items in 32 bits, and 12
-  // workgroups of 512 per 16 tokens would overflow that past S = 11M.
+  // Measured against the persistent kernel: S = 2048 19.9 -> 16.9 us, equal
+  // at 8192; with 3 or 4 splits it was slower beyond S = 1024. Up to S =
+  // 2^20: a dispatch counts its work-items in 32 bits, and 12 workgroups of
+  // 512 per 16 tokens would overflow that past S = 11M. One partial, with an
+  // LSE or without, takes the copy instances (the one-tile one while it
+  // fits, else the persistent kernel's): with an LSE, against merging it in
+  // the one-tile instance as two partials are, S = 4096 26.8 -> 20.2 us,
+  // S = 16384 94.7 -> 64.3 us, S = 256 6.3 -> 5.8 us.
   const bool fits = ntiles <= max(1, cus * WG_PER_CU / NH) && nch == 1;
-  if (fits || (!nolse && n <= 2 && S <= ONE_TILE_SMAX)) {
+  if (fits || (!copy && n <= 2 && S <= ONE_TILE_SMAX)) {
     const int tt = fits ? latency_tile(S, cus) : TILE_T;
-    if (nolse || n <= lat_nmax(tt)) {
+    if (copy || n <= lat_nmax(tt)) {
       p.kernel = MLA_POST_KERNEL_ONE_TILE;
       p.tile_tokens = tt;
       // rows held per token: the fewest instantiated that hold all n (fewer
       // registers, so more workgroups resident at once)
-      p.rows_held = nolse ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= LAT_NMAX ? LAT_NMAX : 2 * LAT_NMAX;
+      p.rows_held = copy ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= LAT_NMAX ? LAT_NMAX : 2 * LAT_NMAX;
       p.lse_chunks = 1;
       p.workgroups_per_head = (S + tt - 1) / tt;
       p.workgroups = NH * p.workgroups_per_head;
       return p;
     }
   }
-  const int stt = nolse ? 0 : split_tile(n, S, cus);
+  const int stt = copy ? 0 : split_tile(n, S, cus);
   if (stt > 0) {
     p.kernel = MLA_POST_KERNEL_SPLIT_ROWS;
     p.tile_tokens = stt;
@@ -1351,17 +1383,17 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
   // 31.2 (n = 2), 45.1 -> 39.4 (n = 4), S = 8192 by 14-30%. Eight rows of
   // each token for n <= 8 needs 141 registers, one resident workgroup per CU,
   // and was 20-30% slower with 6 and 8 splits.
-  p.pair_rows = !nolse && nch == 1 && n <= PF_ROWS / 2 ? PF_ROWS / 2 : 0;
+  p.pair_rows = !copy && nch == 1 && n <= PF_ROWS / 2 ? PF_ROWS / 2 : 0;
   p.workgroups_per_head = wph;
   p.workgroups = NH * wph;
-  tile_counts(S, wph, spread_leftover(nolse, n), p.full_tiles, p.short_tokens);
+  tile_counts(S, wph, spread_leftover(copy, n), p.full_tiles, p.short_tokens);
   return p;
 }
 
-template <bool NOLSE, int TT>
+template <bool COPY, int TT>
 void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
-  if constexpr (NOLSE) {
+  if constexpr (COPY) {
     hipLaunchKernelGGL((mla_post_latency_kernel<true, TT, LAT_NMAX>), grid, block, 0, stream, k);
   } else {
     if (p.rows_held == 2)
@@ -1397,7 +1429,7 @@ int launch_split_chunks(const KArgs& k, const mla_post_plan& p, hipStream_t stre
   }
 }
 
-int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t stream) {
+int launch_plan(const KArgs& k, const mla_post_plan& p, bool copy, hipStream_t stream) {
   if (p.kernel == MLA_POST_KERNEL_SPLIT_ROWS) {
     switch (p.tile_tokens) {
       case 8: return launch_split_chunks<1>(k, p, stream);
@@ -1408,14 +1440,14 @@ int launch_plan(const KArgs& k, const mla_post_plan& p, bool nolse, hipStream_t 
   }
   if (p.kernel == MLA_POST_KERNEL_ONE_TILE) {
     if (p.tile_tokens == TILE_T)
-      nolse ? launch_one_tile<true, TILE_T>(k, p, stream) : launch_one_tile<false, TILE_T>(k, p, stream);
+      copy ? launch_one_tile<true, TILE_T>(k, p, stream) : launch_one_tile<false, TILE_T>(k, p, stream);
     else
-      nolse ? launch_one_tile<true, TILE_T / 2>(k, p, stream) : launch_one_tile<false, TILE_T / 2>(k, p, stream);
+      copy ? launch_one_tile<true, TILE_T / 2>(k, p, stream) : launch_one_tile<false, TILE_T / 2>(k, p, stream);
     return launched(hipGetLastError());
   }
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
   const int wph = p.workgroups_per_head;
-  if (nolse)
+  if (copy)
     hipLaunchKernelGGL((mla_post_kernel<true, 1, 0>), grid, block, 0, stream, k, wph);
   else if (p.pair_rows == PF_ROWS / 2)
     hipLaunchKernelGGL((mla_post_kernel<false, 1, PF_ROWS / 2>), grid, block, 0, stream, k, wph);
@@ -1471,7 +1503,7 @@ int mla_post(const mla_post_args* in, void* stream) {
   k.kv_lens = a->kv_lens;
   k.kl_sj = a->kl_sj;
   k.qsl = a->qsl;
-  return launch_plan(k, make_plan(a, device_cus()), a->lse == nullptr, static_cast<hipStream_t>(stream));
+  return launch_plan(k, make_plan(a, device_cus()), a->n == 1, static_cast<hipStream_t>(stream));
 }
 
 int mla_post_plan_for(const mla_post_args* in, int32_t cus, mla_post_plan* out) {

@@ -268,6 +268,27 @@ def test_split_rows(gpu_lib, n, S, tt, opts):
     full_parity(m, w)
 
 
+@pytest.mark.parametrize("S", [300, 1100], ids=["one_tile", "persistent"])
+def test_one_partial_with_lse_is_copied(gpu_lib, S):
+    """One partial with an LSE is copied, not merged: its weight is 1 or 0.
+    A token whose LSE sanitises to -inf (-inf, NaN, +inf) gives exact zeros
+    although its row holds NaN and inf; every other token's latents are its
+    row bit for bit, except that -0 becomes +0 (as in the merge, whose sum
+    starts at +0); T1-T4 hold against the oracle."""
+    m = gpu_lib
+    w = synth.dense_splits(f"copy_lse_S{S}", 1, S, seed=50, p_neg_inf=0.2, p_nan=0.05, p_pos_inf=0.05)
+    dead = ~np.isfinite(w.lse_view()[0])  # [S, 12]
+    ob = w.o_buf.copy()
+    ob[0][dead] = np.where(np.arange(512) % 2 == 0, 0x7FC0, 0x7F80).astype(np.uint16)
+    ob[0][~dead, ::7] = 0x8000  # -0 in live rows
+    w.o_buf = ob
+    stats, g, _ = full_parity(m, w)
+    expect = np.where(dead[..., None], 0, ob[0])
+    expect = np.where((expect & 0x7FFF) == 0, 0, expect).astype(np.uint16)
+    assert np.array_equal(g["lat"], expect)
+    assert np.all(np.isfinite(O.bf16_to_f64(g["core"])))
+
+
 @pytest.mark.parametrize("n,S", [(4, 33), (20, 33), (20, 400)], ids=["one_tile_instance", "split_rows", "persistent"])
 def test_strided_weights_and_lse(gpu_lib, n, S):
     """W_V codes as a column slice of a wider buffer, scales stored with the

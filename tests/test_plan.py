@@ -59,7 +59,7 @@ TABLE = [
     ((16, 512, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16, workgroups_per_head=64, workgroups=768)),
     ((8, 513, True), dict(kernel="one_tile", tile_tokens=16, rows_held=8, workgroups_per_head=33)),
     ((4, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=4, workgroups_per_head=64)),
-    ((1, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=64)),
+    ((1, 1024, True), dict(kernel="one_tile", tile_tokens=16, rows_held=1, workgroups_per_head=64)),
     ((3, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=4)),
     ((5, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=8)),
     ((9, 100, True), dict(kernel="one_tile", tile_tokens=8, rows_held=16)),
@@ -70,11 +70,14 @@ TABLE = [
     # both tokens' rows a tile ahead for n <= 4 with LSEs
     ((3, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
     ((4, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
-    # one or two partials with LSEs: the one-tile instance at every size
-    ((1, 4096, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=256)),
+    # two partials with LSEs: the one-tile instance at every size up to 2^20
     ((2, 8200, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=513)),
-    ((1, 1 << 20, True), dict(kernel="one_tile", tile_tokens=16, workgroups_per_head=65536)),
-    ((1, (1 << 20) + 16, True), dict(kernel="persistent", workgroups_per_head=64)),
+    ((2, 1 << 20, True), dict(kernel="one_tile", tile_tokens=16, workgroups_per_head=65536)),
+    ((2, (1 << 20) + 16, True), dict(kernel="persistent", workgroups_per_head=64)),
+    # one partial, with an LSE or not, is copied: as without LSEs, the
+    # one-tile instance while it fits, else the persistent kernel
+    ((1, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
+    ((1, 1 << 20, True), dict(kernel="persistent", workgroups_per_head=64)),
     ((5, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
     # the one-round rule (65 to 96 tiles) and the leftover deal
     ((16, 1100, True), dict(kernel="persistent", workgroups_per_head=40, workgroups=480, full_tiles=1, short_tokens=12)),
@@ -136,7 +139,7 @@ def test_routing_table_at_256_cus(key, expect):
         assert p["workgroups"] == 12 * p["workgroups_per_head"]
     else:
         assert p["tile_tokens"] == 16 and p["rows_held"] == 0
-        assert p["pair_rows"] == (4 if key[2] and key[0] <= 4 else 0)
+        assert p["pair_rows"] == (4 if key[2] and 2 <= key[0] <= 4 else 0)
 
 
 def test_empty_batch_launches_nothing():
