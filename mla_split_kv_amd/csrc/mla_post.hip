@@ -585,8 +585,9 @@ __host__ __device__ inline void tile_counts(int S, int k, bool spread, int& main
   chunk = spread ? (rest + k - 1) / k : (rest < TILE_T ? rest : TILE_T);
 }
 
-// Whether leftover tokens are dealt out evenly (see TileSched).
-__host__ __device__ inline bool spread_leftover(bool nolse, int n) { return nolse || n >= SPREAD_MIN_N; }
+// Whether leftover tokens are dealt out evenly (see TileSched): for one
+// partial (copied) and from SPREAD_MIN_N partials.
+__host__ __device__ inline bool spread_leftover(bool copy, int n) { return copy || n >= SPREAD_MIN_N; }
 
 __device__ __forceinline__ TileSched tile_sched(int S, int k, int slot, bool spread) {
   TileSched t;
@@ -1288,7 +1289,7 @@ int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
 // Tokens per workgroup of the split-rows kernel for a call with LSEs, or 0
 // when the call does not take it: more partials than the one-tile instance
 // holds, and at most half as many 16-token tiles as CUs (S <= 160 at 256
-// CUs). The tile (8, 4, 2 or 1 tokens; at most SPLIT_NB batches of rows per
+// CUs), 9/16 as many with 64 partials or more (S <= 192). The tile (8, 4, 2 or 1 tokens; at most SPLIT_NB batches of rows per
 // wave) is the one whose busiest CU finishes first by a simple model: a CU
 // runs ceil(grid / CUs) workgroups one after another, each costing a fixed
 // SPLIT_ROUND_ROWS plus its tile's token rows (TT n). On a tie, the larger
@@ -1301,12 +1302,15 @@ int lse_chunks(int n) { return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8; }
 // 171.0 -> 21.8 (512); S = 160 13.1 -> 9.4 (17), 29.4 -> 20.0 (64), 212.4
 // -> 163.3 (512). Past S = 160 the persistent kernel is 5-11% ahead with up
 // to 32 splits (S = 176: 13.1 against 14.4 us with 17); with 64 to 512 the
-// split-rows kernel stays 2-11% ahead up to S = 192 and within 2% either
-// way at S = 256, so one bound serves all.
+// split-rows kernel is ahead or level up to S = 192 (S = 161, one round of
+// 8-token tiles: 28.2 -> 19.4 us with 64, 52.2 -> 39.0 with 128; S = 176:
+// 29.2 -> 28.7 with 64, level with 128, 208.9 -> 186.6 with 512) and within
+// 2% either way at S = 256.
 constexpr int SPLIT_ROUND_ROWS = 150;
 int split_tile(int n, int S, int cus) {
   const int64_t ntiles = (S + TILE_T - 1) / TILE_T;
-  if (n <= 2 * LAT_NMAX || 2 * NH * ntiles > cus) return 0;
+  const int64_t bound = (n >= 64 ? 9 : 8) * (int64_t)cus;  // 16 x 12 x tiles at most
+  if (n <= 2 * LAT_NMAX || 16 * NH * ntiles > bound) return 0;
   const int nch = lse_chunks(n);
   int cap = WAVES;
   while (cap > 1 && split_batches(WAVES / cap, nch) > SPLIT_NB) cap /= 2;

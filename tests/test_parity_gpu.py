@@ -252,6 +252,8 @@ SPLIT_ROWS = [
     (512, 1, 1, dict(p_neg_inf=0.02)),
     # tokens all of whose partials are dead: exact zeros
     (24, 150, 8, dict(p_neg_inf=0.9)),
+    # past S = 160 with 64 splits or more (up to S = 192)
+    (64, 190, 4, dict(p_neg_inf=0.1)),
 ]
 
 

@@ -122,7 +122,10 @@ TABLE = [
     ((200, 5, True), dict(kernel="split_rows", tile_tokens=1, lse_chunks=4)),
     ((512, 2, True), dict(kernel="split_rows", tile_tokens=1, rows_held=16, lse_chunks=8, workgroups_per_head=2,
                           workgroups=24)),
-    ((512, 161, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=11)),
+    # the split-rows bound: S <= 160 below 64 splits, S <= 192 from 64
+    ((63, 161, True), dict(kernel="persistent", workgroups_per_head=11)),
+    ((64, 192, True), dict(kernel="split_rows", tile_tokens=4, lse_chunks=1, workgroups_per_head=48)),
+    ((512, 193, True), dict(kernel="persistent", lse_chunks=8, workgroups_per_head=13)),
 ]
 
 
@@ -214,16 +217,17 @@ def split_model(n, S, cus):
 
 def test_split_rows_rule():
     """Over n and S at several CU counts: the split-rows kernel exactly when
-    n > 16 with LSEs and 2 x 12 x ceil(S / 16) <= CUs, with the tile and LSE
-    chunks of the model and the rows a wave holds at once."""
+    n > 16 with LSEs and 16 x 12 x ceil(S / 16) <= 8 CUs (9 CUs from 64
+    splits), with the tile and LSE chunks of the model and the rows a wave
+    holds at once."""
     for cus in (256, 304, 80, 32):
         for n in (1, 2, 16, 17, 31, 32, 33, 64, 65, 100, 128, 129, 256, 257, 512):
-            for S in (1, 2, 3, 5, 16, 22, 31, 32, 33, 43, 63, 64, 86, 100, 144, 160, 161, 176, 250, 336):
+            for S in (1, 2, 3, 5, 16, 22, 31, 32, 33, 43, 63, 64, 86, 100, 144, 160, 161, 176, 192, 193, 250, 336):
                 for lse in (True, False):
                     if not lse and n > 1:
                         continue
                     p = plan(n, S, lse, cus)
-                    want = lse and n > 16 and 24 * -(-S // 16) <= cus
+                    want = lse and n > 16 and 16 * 12 * -(-S // 16) <= (9 if n >= 64 else 8) * cus
                     assert (p["kernel"] == "split_rows") == want, (n, S, cus, p)
                     if not want:
                         continue
