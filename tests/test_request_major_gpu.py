@@ -100,6 +100,23 @@ def test_split_rows_masks(gpu_lib, per, q, S, end, tt):
     assert np.all(g["core"][end:] == 0) and np.all(g["lat"][end:] == 0)
 
 
+@pytest.mark.parametrize("S", [40, 1104], ids=["one_tile", "persistent"])
+def test_one_partial_with_lse_masks(gpu_lib, S):
+    """One partial per request with LSEs (copied, not merged) under push-side
+    masks: partials of requests with no KV and tokens past the batch give
+    +0; every other token meets T1-T4, on both copy routes."""
+    m = gpu_lib
+    w = synth.request_major(f"rm_copy_S{S}", per=1, q=4, S=S, seed=60 + S % 7, compact=True, kv_zero=0.3,
+                            batch_rows=S - 7)
+    d = device_inputs(w)
+    p = m.plan(d["o"], d["lse"], d["w_v"], d["w_v_scale"], d["gate"], **d["layout"])
+    assert p["kernel"] == ("one_tile" if S == 40 else "persistent"), p
+    g, ref, _ = check(m, w)
+    assert np.all(g["core"][S - 7:] == 0) and np.all(g["lat"][S - 7:] == 0)
+    dead = np.repeat(w.kv_lens[0] == 0, 4)
+    assert np.all(g["lat"][dead] == 0)
+
+
 def test_shared_kv_row_dense_splits(gpu_lib):
     """Dense split partials with one shared row of KV lengths ([S // q]) and
     q = 4: a request with no KV yields +0 for its tokens."""
