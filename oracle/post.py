@@ -157,6 +157,9 @@ def merge_values(o, lse):
     [mla_back: combine_splits] relies on empty splits holding zeros; one rule
     covers both).
 
+    The sum starts at +0, as the page's float32 accumulators do, so a merge
+    whose terms are all zero (every weight 0, or live rows holding +-0) is +0.
+
     Returns (x, mag): x [T, 12, K] float64, and mag = sum_j w_j |o_j[k]|, the
     size of the terms the merge cancels (used by tolerances).
     """
@@ -165,7 +168,7 @@ def merge_values(o, lse):
     w = np.moveaxis(w, -1, 0)[..., None]  # [N, T, 12, 1]
     live = w > 0.0
     oz = np.where(live, o, 0.0)
-    x = np.where(live, w * oz, 0.0).sum(axis=0)
+    x = 0.0 + np.where(live, w * oz, 0.0).sum(axis=0)
     mag = np.where(live, w * np.abs(oz), 0.0).sum(axis=0)
     return x, mag
 
@@ -428,10 +431,16 @@ def mla_post(o_bits, lse, w_codes, w_scales, gate_bits, tokens=None) -> dict:
 
 
 def ulp_bf16(a) -> np.ndarray:
-    """Spacing of bf16 values at magnitude |a| (float64): 2^(e - 7) for a in
-    [2^e, 2^(e+1)), 2^-133 in the subnormal range."""
+    """Spacing of bf16 values at magnitude |a| (float64): 2^(e - 7) for |a| in
+    [2^e, 2^(e+1)) with e >= -126, and 2^-133 below 2^-126 (the subnormal
+    range, zero included). Used by the acceptance tolerances.
+
+    ``np.frexp`` gives exponent 0 for a zero input, which would read as the
+    spacing at 0.5; zero takes the subnormal spacing explicitly.
+    """
     a = np.abs(np.asarray(a, dtype=np.float64))
     _, e = np.frexp(a)
+    e = np.where(a == 0.0, -133 + 8, e)
     return np.ldexp(1.0, np.maximum(e - 8, -133))
 
 

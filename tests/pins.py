@@ -556,6 +556,26 @@ def pin_gate_core():
     assert np.all(hand == 0x4380)
 
 
+def pin_ulp_bf16_brute():
+    """The tolerance helper's bf16 spacing against the gaps between adjacent
+    bf16 values: for every non-negative finite bf16 pattern b, the value of
+    b + 1 minus the value of b (past the largest finite value, the gap to
+    2^128), at the value itself, strictly inside the gap (its midpoint) and
+    for the negative value; zero has the smallest subnormal's spacing,
+    2^-133."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)  # +0 .. the largest finite value
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    nxt = np.append(vals[1:], 2.0**128)
+    gap = nxt - vals
+    assert np.array_equal(O.ulp_bf16(vals), gap)
+    assert np.array_equal(O.ulp_bf16(vals + gap / 2), gap)
+    assert np.array_equal(O.ulp_bf16(-vals), gap)
+    assert O.ulp_bf16(0.0) == 2.0**-133 and O.ulp_bf16(-0.0) == 2.0**-133
+    # hand values: 1 and 1.5 lie in [1, 2), spacing 2^-7; 2 starts the next binade
+    assert np.array_equal(O.ulp_bf16(np.array([1.0, 1.5, 2.0, 2.0**-126, 2.0**-130])),
+                          np.array([2.0**-7, 2.0**-7, 2.0**-6, 2.0**-133, 2.0**-133]))
+
+
 def pin_end_to_end_small():
     """The whole oracle on a tiny case equals a scalar walk-through built from
     the pinned pieces (BLAS for the contraction), per token and head."""
@@ -577,8 +597,11 @@ def pin_end_to_end_small():
             assert np.array_equal(lat, r["lat"][t, h])
             lc, lsc = O.quantize_mxfp4(lat[None])
             acc = Wd[h] @ O.dequant_mxfp4(lc, lsc)[0]
+            # the float64 BLAS sum of the dequantised products is exact here:
+            # every product is a multiple of the smallest block's quantum and
+            # the blocks' scales span far less than 53 bits
             core = O.rne_bf16(O.bf16_to_f64(O.rne_bf16(acc)) * O.bf16_to_f64(g[t, 128 * h : 128 * h + 128]))
-            assert np.mean(core == r["core"][t, 128 * h : 128 * h + 128]) > 0.99
+            assert np.array_equal(core, r["core"][t, 128 * h : 128 * h + 128])
 
 
 def pin_request_major_gather():
@@ -659,6 +682,7 @@ ALL_PINS = [
     pin_wuv_one_hot,
     pin_gate_core,
     pin_end_to_end_small,
+    pin_ulp_bf16_brute,
     pin_request_major_gather,
     pin_push_mask,
 ]

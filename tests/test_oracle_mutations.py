@@ -142,6 +142,19 @@ def _push_mask_token_index(lse, q, kv_lens=None, qsl=None):
     return v
 
 
+def _ulp_frexp_at_zero(a):
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    _, e = np.frexp(a)  # exponent 0 for a zero input: reads as the spacing at 0.5
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def _ulp_exponent_off_by_one(a):
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    _, e = np.frexp(a)
+    e = np.where(a == 0.0, -125, e)
+    return np.ldexp(1.0, np.maximum(e - 7, -133))
+
+
 MUTATIONS = [
     ("sanitize misses +inf", "sanitize_lse", _sanitize_no_posinf, [pins.pin_nan_inf_as_neg_inf]),
     ("sanitize misses NaN", "sanitize_lse", _sanitize_no_nan, [pins.pin_nan_inf_as_neg_inf]),
@@ -161,6 +174,8 @@ MUTATIONS = [
     ("gate columns transposed", "gate_core", _gate_transposed, [pins.pin_gate_core]),
     ("request index off by one", "gather_request_major", _gather_shifted, [pins.pin_request_major_gather]),
     ("mask uses token not request", "push_mask", _push_mask_token_index, [pins.pin_push_mask]),
+    ("ulp of zero from frexp", "ulp_bf16", _ulp_frexp_at_zero, [pins.pin_ulp_bf16_brute]),
+    ("ulp exponent off by one", "ulp_bf16", _ulp_exponent_off_by_one, [pins.pin_ulp_bf16_brute]),
 ]
 
 
