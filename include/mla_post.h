@@ -23,10 +23,14 @@
  *
  * All entry points are host functions with C linkage. Device pointers are
  * caller-owned device memory; the library keeps no pointer after a call
- * returns, allocates nothing per call and holds no mutable global state, so
- * calls are thread-safe. Work is enqueued asynchronously on the caller's HIP
- * stream. Validation failures are reported synchronously, launch nothing and
- * leave every output untouched.
+ * returns and allocates nothing per call. Its only mutable global state is a
+ * per-device cache of the compute-unit count (asked of the runtime on first
+ * use, then only read; atomic) and a per-thread copy of the last HIP launch
+ * error's message (mla_post_last_hip_error). Neither carries data from one
+ * call into another's results, so calls are thread-safe, and calls on
+ * different streams may run at the same time. Work is enqueued
+ * asynchronously on the caller's HIP stream. Validation failures are
+ * reported synchronously, launch nothing and leave every output untouched.
  */
 #ifndef MLA_POST_H
 #define MLA_POST_H

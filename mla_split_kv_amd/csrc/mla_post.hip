@@ -767,11 +767,11 @@ __global__ __launch_bounds__(THREADS) void mla_post_kernel(const KArgs a, int wg
       acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
       acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
     }
-    // The MFMAs read operands from all 64 lanes: they must run with the whole
-    // wave active. Pinning the result here keeps the compiler from sinking
-    // them into the per-lane store condition below (where a ragged tile masks
-    // lanes).
-    asm volatile("" : "+v"(acc));
+    // The MFMAs read operands from all 64 lanes, so they must run with the
+    // whole wave active: their result goes straight to an unconditional LDS
+    // store below, before any lane-dependent branch, so no lane condition can
+    // enclose them (a CPU test checks the built code for MFMAs under a
+    // narrowed exec mask).
 
     // ---- gate and stage ([mla_back: stage_uv]): the lane holds rows
     // v0..v0+3 (v0 = 16 wave + 4 kb) of token tl. The finished core values
@@ -838,7 +838,8 @@ __device__ __forceinline__ void tile_wuv_store(const KArgs& a, int wave, int tl,
     acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
     acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
   }
-  asm volatile("" : "+v"(acc));  // MFMAs with the whole wave active (see the main kernel)
+  // the result is stored unconditionally before any lane-dependent branch, so
+  // the MFMAs run with the whole wave active (see the persistent kernel)
   *reinterpret_cast<uint2*>(s_out + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
       make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
   __syncthreads();
@@ -1273,6 +1274,22 @@ int launched(hipError_t e) {
   return MLA_POST_OK;
 }
 
+template <class T>
+struct same_type {
+  using type = T;
+};
+
+// Enqueue kernel k and report this launch's own status: hipLaunchKernel
+// returns the error of this launch, so an error left pending by an earlier
+// HIP call (the caller's, or a device query) is neither taken for it nor
+// cleared. The arguments are converted to the kernel's parameter types
+// before their addresses are taken.
+template <typename... P>
+int launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t stream, typename same_type<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return launched(hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, stream));
+}
+
 // Tokens per workgroup of the one-tile instance: 8 while that grid stays
 // within 3 workgroups per CU, else 16 (with n > 8 the call then goes to the
 // persistent kernel). Measured at 256 CUs with n = 4, 8 and 16: 8-token tiles
@@ -1395,19 +1412,17 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
 }
 
 template <bool COPY, int TT>
-void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
+int launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
   if constexpr (COPY) {
-    hipLaunchKernelGGL((mla_post_latency_kernel<true, TT, LAT_NMAX>), grid, block, 0, stream, k);
+    return launch(mla_post_latency_kernel<true, TT, LAT_NMAX>, grid, block, stream, k);
   } else {
-    if (p.rows_held == 2)
-      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, 2>), grid, block, 0, stream, k);
-    else if (p.rows_held == 4)
-      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, 4>), grid, block, 0, stream, k);
-    else if (p.rows_held == LAT_NMAX)
-      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, LAT_NMAX>), grid, block, 0, stream, k);
-    else if constexpr (lat_nmax(TT) > LAT_NMAX)
-      hipLaunchKernelGGL((mla_post_latency_kernel<false, TT, 2 * LAT_NMAX>), grid, block, 0, stream, k);
+    if (p.rows_held == 2) return launch(mla_post_latency_kernel<false, TT, 2>, grid, block, stream, k);
+    if (p.rows_held == 4) return launch(mla_post_latency_kernel<false, TT, 4>, grid, block, stream, k);
+    if (p.rows_held == LAT_NMAX) return launch(mla_post_latency_kernel<false, TT, LAT_NMAX>, grid, block, stream, k);
+    if constexpr (lat_nmax(TT) > LAT_NMAX)
+      return launch(mla_post_latency_kernel<false, TT, 2 * LAT_NMAX>, grid, block, stream, k);
+    return MLA_POST_EUNSUPPORTED;
   }
 }
 
@@ -1416,8 +1431,7 @@ void launch_one_tile(const KArgs& k, const mla_post_plan& p, hipStream_t stream)
 template <int G, int NCH>
 int launch_split(const KArgs& k, const mla_post_plan& p, hipStream_t stream) {
   if constexpr (split_batches(G, NCH) <= SPLIT_NB) {
-    hipLaunchKernelGGL((mla_post_split_kernel<G, NCH>), dim3((unsigned)p.workgroups), dim3(THREADS), 0, stream, k);
-    return launched(hipGetLastError());
+    return launch(mla_post_split_kernel<G, NCH>, dim3((unsigned)p.workgroups), dim3(THREADS), stream, k);
   } else {
     return MLA_POST_EUNSUPPORTED;
   }
@@ -1444,26 +1458,17 @@ int launch_plan(const KArgs& k, const mla_post_plan& p, bool copy, hipStream_t s
   }
   if (p.kernel == MLA_POST_KERNEL_ONE_TILE) {
     if (p.tile_tokens == TILE_T)
-      copy ? launch_one_tile<true, TILE_T>(k, p, stream) : launch_one_tile<false, TILE_T>(k, p, stream);
-    else
-      copy ? launch_one_tile<true, TILE_T / 2>(k, p, stream) : launch_one_tile<false, TILE_T / 2>(k, p, stream);
-    return launched(hipGetLastError());
+      return copy ? launch_one_tile<true, TILE_T>(k, p, stream) : launch_one_tile<false, TILE_T>(k, p, stream);
+    return copy ? launch_one_tile<true, TILE_T / 2>(k, p, stream) : launch_one_tile<false, TILE_T / 2>(k, p, stream);
   }
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
   const int wph = p.workgroups_per_head;
-  if (copy)
-    hipLaunchKernelGGL((mla_post_kernel<true, 1, 0>), grid, block, 0, stream, k, wph);
-  else if (p.pair_rows == PF_ROWS / 2)
-    hipLaunchKernelGGL((mla_post_kernel<false, 1, PF_ROWS / 2>), grid, block, 0, stream, k, wph);
-  else if (p.lse_chunks == 1)
-    hipLaunchKernelGGL((mla_post_kernel<false, 1, 0>), grid, block, 0, stream, k, wph);
-  else if (p.lse_chunks == 2)
-    hipLaunchKernelGGL((mla_post_kernel<false, 2, 0>), grid, block, 0, stream, k, wph);
-  else if (p.lse_chunks == 4)
-    hipLaunchKernelGGL((mla_post_kernel<false, 4, 0>), grid, block, 0, stream, k, wph);
-  else
-    hipLaunchKernelGGL((mla_post_kernel<false, 8, 0>), grid, block, 0, stream, k, wph);
-  return launched(hipGetLastError());
+  if (copy) return launch(mla_post_kernel<true, 1, 0>, grid, block, stream, k, wph);
+  if (p.pair_rows == PF_ROWS / 2) return launch(mla_post_kernel<false, 1, PF_ROWS / 2>, grid, block, stream, k, wph);
+  if (p.lse_chunks == 1) return launch(mla_post_kernel<false, 1, 0>, grid, block, stream, k, wph);
+  if (p.lse_chunks == 2) return launch(mla_post_kernel<false, 2, 0>, grid, block, stream, k, wph);
+  if (p.lse_chunks == 4) return launch(mla_post_kernel<false, 4, 0>, grid, block, stream, k, wph);
+  return launch(mla_post_kernel<false, 8, 0>, grid, block, stream, k, wph);
 }
 
 }  // namespace
@@ -1543,9 +1548,8 @@ int mla_quantize_mxfp4(const void* x, int64_t rows, int32_t cols, int64_t x_stri
   // at most 2^16 workgroups, each wave striding over the rows: the grid's
   // work-item count must fit the 32 bits of a dispatch
   const int64_t blocks = std::min<int64_t>((rows + QWAVES - 1) / QWAVES, QMAX_BLOCKS);
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint8_t*>(x), rows, cols, x_stride * 2, codes, c_stride, scales, s_stride);
-  return launched(hipGetLastError());
+  return launch(quantize_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), static_cast<hipStream_t>(stream),
+                static_cast<const uint8_t*>(x), rows, cols, (int64_t)(x_stride * 2), codes, c_stride, scales, s_stride);
 }
 
 const char* mla_post_strerror(int status) {
