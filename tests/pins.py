@@ -662,6 +662,69 @@ def pin_push_mask():
     assert np.array_equal(O.push_mask(lse, q), lse.astype(np.float64))  # no masks: unchanged
 
 
+# ---------------------------------------------------------------- o_proj
+
+
+def _oproj_case(rng, S, D, K, sigma=1.0):
+    core = bf16_bits_from_f32(rng.standard_normal((S, K)) * sigma)
+    w = bf16_bits_from_f32(rng.standard_normal((D, K)) / np.sqrt(K))
+    return core, w
+
+
+def pin_oproj_exact_rational():
+    """o_proj against exact rational arithmetic: every output of a small
+    case is the exact sum of its K products of bf16 values (Fractions),
+    rounded to bf16 by search over every bf16 value; includes a case whose
+    products span more than 37 binades (values from 2^-40 to 2^30)."""
+    from oracle.oproj import oproj
+
+    rng = np.random.default_rng(40)
+    cases = [_oproj_case(rng, 3, 5, 64)]
+    core = bf16_bits_from_f32(rng.standard_normal((2, 32)) * np.exp2(rng.integers(-40, 30, size=(2, 32))))
+    w = bf16_bits_from_f32(rng.standard_normal((3, 32)))
+    cases.append((core, w))
+    for core, w in cases:
+        r = oproj(core, w)
+        a, b = O.bf16_to_f64(core), O.bf16_to_f64(w)
+        for t in range(core.shape[0]):
+            for d in range(w.shape[0]):
+                exact = sum((Fraction(float(a[t, k])) * Fraction(float(b[d, k])) for k in range(core.shape[1])), Fraction(0))
+                assert int(r["out"][t, d]) == brute_rne_bf16(exact), (t, d)
+                assert abs(Fraction(float(r["y"][t, d])) - exact) <= Fraction(1, 2**50) * abs(Fraction(float(r["mag"][t, d])))
+
+
+def pin_oproj_known_answers():
+    """One-hot rows of W_O pick a column of core exactly (row d of W_O = 1.0
+    at k = (7 d) mod K); a zero core row gives +0; doubling core doubles
+    every output; out[t, d] takes row t of core and row d of W_O (a
+    transposed operand fails on a non-square case)."""
+    from oracle.oproj import oproj
+
+    rng = np.random.default_rng(41)
+    S, D, K = 4, 6, 96
+    core, w = _oproj_case(rng, S, D, K)
+    core[2] = 0
+    one = np.zeros((D, K), np.uint16)
+    for d in range(D):
+        one[d, (7 * d) % K] = 0x3F80
+    r = oproj(core, one)
+    for d in range(D):
+        assert np.array_equal(r["out"][:, d], core[:, (7 * d) % K])
+    r = oproj(core, w)
+    assert np.all(r["out"][2] == 0)
+    c2 = O.rne_bf16(2.0 * O.bf16_to_f64(core))
+    assert np.array_equal(O.bf16_to_f64(oproj(c2, w)["out"]), 2.0 * O.bf16_to_f64(r["out"]))
+    # a row of W_O with a single 2.0 at k = 0 and a core row of ones except
+    # k = 0: only the product at k = 0 counts
+    w2 = np.zeros((D, K), np.uint16)
+    w2[3, 0] = 0x4000
+    c3 = np.full((S, K), 0x3F80, np.uint16)
+    c3[:, 0] = O.rne_bf16(np.arange(S, dtype=np.float64) + 1)
+    r3 = oproj(c3, w2)
+    assert np.array_equal(O.bf16_to_f64(r3["out"][:, 3]), 2.0 * (np.arange(S) + 1))
+    assert np.all(r3["out"][:, [0, 1, 2, 4, 5]] == 0)
+
+
 ALL_PINS = [
     pin_textbook_attention,
     pin_single_partial_identity,
@@ -685,4 +748,6 @@ ALL_PINS = [
     pin_ulp_bf16_brute,
     pin_request_major_gather,
     pin_push_mask,
+    pin_oproj_exact_rational,
+    pin_oproj_known_answers,
 ]

@@ -9,6 +9,10 @@ import pins
 
 _orig = {n: getattr(O, n) for n in dir(O) if callable(getattr(O, n))}
 
+import oracle.oproj as OP  # noqa: E402
+
+_orig_oproj = OP.oproj
+
 
 def _sanitize_no_posinf(lse):
     v = np.asarray(lse, dtype=np.float64).copy()
@@ -155,6 +159,24 @@ def _ulp_exponent_off_by_one(a):
     return np.ldexp(1.0, np.maximum(e - 7, -133))
 
 
+def _oproj_w_transposed(core_bits, w_bits, rows=None):
+    w = np.asarray(w_bits)
+    return _orig_oproj(core_bits, w.reshape(w.shape[1], w.shape[0]).T.copy(), rows)
+
+
+def _oproj_truncated(core_bits, w_bits, rows=None):
+    r = _orig_oproj(core_bits, w_bits, rows)
+    f = r["y"].astype(np.float32)
+    r["out"] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    return r
+
+
+def _oproj_f32_products(core_bits, w_bits, rows=None):
+    r = _orig_oproj(core_bits, w_bits, rows)
+    r["out"] = O.rne_bf16(r["y"].astype(np.float16).astype(np.float64))  # a half-precision sum
+    return r
+
+
 MUTATIONS = [
     ("sanitize misses +inf", "sanitize_lse", _sanitize_no_posinf, [pins.pin_nan_inf_as_neg_inf]),
     ("sanitize misses NaN", "sanitize_lse", _sanitize_no_nan, [pins.pin_nan_inf_as_neg_inf]),
@@ -178,10 +200,29 @@ MUTATIONS = [
     ("ulp exponent off by one", "ulp_bf16", _ulp_exponent_off_by_one, [pins.pin_ulp_bf16_brute]),
 ]
 
+OPROJ_MUTATIONS = [
+    ("W_O read transposed", _oproj_w_transposed, [pins.pin_oproj_known_answers]),
+    ("o_proj rounded by truncation", _oproj_truncated, [pins.pin_oproj_exact_rational]),
+    ("o_proj summed in half precision", _oproj_f32_products, [pins.pin_oproj_exact_rational]),
+]
+
 
 @pytest.mark.parametrize("name,attr,fn,catchers", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_mutation_is_caught(monkeypatch, name, attr, fn, catchers):
     monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in catchers:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake '{name}' passed every pin in {[p.__name__ for p in catchers]}"
+
+
+@pytest.mark.parametrize("name,fn,catchers", OPROJ_MUTATIONS, ids=[m[0] for m in OPROJ_MUTATIONS])
+def test_oproj_mutation_is_caught(monkeypatch, name, fn, catchers):
+    monkeypatch.setattr(OP, "oproj", fn)
     caught = []
     for pin in catchers:
         try:
