@@ -354,6 +354,47 @@ def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16)
     return {"size_sweep": rows, "workload": f"{splits} splits, large decode distributions, first S tokens", "steps": steps}
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD's published figure
+
+
+def oproj_bench(core, D: int, steps: int, warmup: int, m, torch) -> dict:
+    """o_proj (include/mla_oproj.h) on the call's own core [S, 1536] with a
+    seeded W_O ~ N(0, 1/sqrt(1536)) bf16 [D, 1536]: microseconds per call
+    from HIP events, TFLOP/s against the bf16 matrix-core peak, and torch's
+    own bf16 matrix product (the vendor BLAS) on the same operands, timed
+    the same way, for context."""
+    import numpy as np
+
+    import synth
+
+    S, K = int(core.shape[0]), int(core.shape[1])
+    rng = np.random.default_rng(99)
+    wo_bits = synth.f32_to_bf16_bits(rng.standard_normal((D, K), dtype=np.float32) / np.float32(np.sqrt(K)))
+    w_o = torch.from_numpy(wo_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.empty((S, D), dtype=torch.bfloat16, device="cuda")
+    call = m.PreparedOproj(core, w_o, out)
+    t = time_gpu(call, steps, warmup, torch)
+    us = 1e3 * t["event_ms"] / steps
+    flops = 2.0 * S * D * K
+    tflops = flops / (us * 1e-6) / 1e12
+    w_t = w_o.t().contiguous()  # [K, D]: a plain 2-D product of contiguous operands
+    ref_out = torch.empty_like(out)
+    tb = time_gpu(lambda: torch.mm(core, w_t, out=ref_out), steps, warmup, torch)
+    us_blas = 1e3 * tb["event_ms"] / steps
+    byts = (S * K + D * K + S * D) * 2
+    return {
+        "workload": f"core [{S}, {K}] (the call's own) x W_O [{D}, {K}]^T -> bf16 [{S}, {D}]",
+        "us_per_call": round(us, 3),
+        "tflops": round(tflops, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "hbm_bytes_min": byts,
+        "vendor_blas_us": round(us_blas, 3),
+        "vs_vendor_blas": round(us_blas / us, 3),
+        "plan": m.oproj_plan(S, D),
+    }
+
+
 def calibrate_copy(torch) -> None:
     """A plain device-to-device copy of 1 GiB (torch dispatches it to the HIP
     runtime copy kernel __amd_rocclr_copyBuffer): counter
@@ -385,6 +426,8 @@ def main() -> int:
         "--cpu-workers", type=int, default=0, help="processes for the all-cores oracle timing (default min(16, CPUs); 1 skips it)"
     )
     ap.add_argument("--all", action="store_true", help="also time the four other standard workloads (stderr)")
+    ap.add_argument("--oproj-d", type=int, default=7168,
+                    help="also time o_proj on the call's core with this output width (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--sizes", help="comma-separated batch sizes S: print a size sweep (one JSON object) instead")
     ap.add_argument("--splits", type=int, default=16, help="partials per (token, head) of the size sweep")
@@ -454,6 +497,11 @@ def main() -> int:
     tokens_per_s = w.S * args.steps / t["wall_s"]
 
     copy_gbps = copy_ceiling(torch)
+    op = None
+    if args.oproj_d > 0:
+        log(f"timing o_proj on the call's core, D = {args.oproj_d}")
+        op = oproj_bench(d["core"], args.oproj_d, args.steps, args.warmup, m, torch)
+        log(f"o_proj: {op}")
     extra = {}
     if args.all:
         scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB, for cold calls
@@ -541,6 +589,8 @@ def main() -> int:
             "what": "plain 1 GiB device copy, bytes read + written per second",
         },
     }
+    if op:
+        out["oproj"] = op
     if cpu_all:
         out["cpu_baseline_all_cores"] = cpu_all
     if extra:

@@ -106,6 +106,9 @@ EXPORTS = (
     "mla_post_strerror",
     "mla_post_last_hip_error",
     "mla_post_version",
+    "mla_oproj",
+    "mla_oproj_check",
+    "mla_oproj_plan",
 )
 
 _lib = None
@@ -149,6 +152,13 @@ def load() -> ctypes.CDLL:
     lib.mla_post_last_hip_error.restype = ctypes.c_char_p
     lib.mla_post_version.argtypes = []
     lib.mla_post_version.restype = ctypes.c_int
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.mla_oproj.argtypes = [vp, i64, i32, i32, vp, i64, i32, vp, i64, vp]
+    lib.mla_oproj.restype = ctypes.c_int
+    lib.mla_oproj_check.argtypes = [vp, i64, i32, i32, vp, i64, i32, vp, i64]
+    lib.mla_oproj_check.restype = ctypes.c_int
+    lib.mla_oproj_plan.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mla_oproj_plan.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -383,3 +393,59 @@ def quantize_mxfp4(x):
     )
     _raise(lib, st)
     return codes, scales
+
+
+# ---------------------------------------------------------------- o_proj (include/mla_oproj.h)
+
+
+def _oproj_args(core, w_o, out):
+    _need(core.dtype == torch.bfloat16 and core.dim() == 2 and core.stride(1) == 1, TypeError,
+          "core must be bf16 [S, K] with unit innermost stride")
+    _need(w_o.dtype == torch.bfloat16 and w_o.dim() == 2 and w_o.stride(1) == 1, TypeError,
+          "w_o must be bf16 [D, K] with unit innermost stride")
+    S, K = int(core.shape[0]), int(core.shape[1])
+    D = int(w_o.shape[0])
+    _need(int(w_o.shape[1]) == K, ValueError, f"w_o must be [D, {K}], got {tuple(w_o.shape)}")
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (S, D) and out.stride(1) == 1, ValueError,
+          f"out must be bf16 [{S}, {D}] with unit innermost stride")
+    _need(core.device == w_o.device == out.device, ValueError, "all tensors must be on one device")
+    return (ctypes.c_void_p(core.data_ptr()), core.stride(0), S, K, ctypes.c_void_p(w_o.data_ptr()), w_o.stride(0), D,
+            ctypes.c_void_p(out.data_ptr()), out.stride(0))
+
+
+def oproj(core, w_o, out=None):
+    """o_proj on torch's current stream: out [S, D] = bf16(core [S, K] @ w_o[D, K]^T)
+    (include/mla_oproj.h); returns out."""
+    lib = load()
+    if out is None:
+        out = torch.empty((int(core.shape[0]), int(w_o.shape[0])), dtype=torch.bfloat16, device=core.device)
+    args = _oproj_args(core, w_o, out)
+    _need(core.is_cuda, ValueError, "tensors must be on a GPU")
+    _raise(lib, lib.mla_oproj(*args, ctypes.c_void_p(_stream(core.device))))
+    return out
+
+
+def oproj_plan(S: int, D: int, cus: int = 0) -> dict:
+    """The tile and grid mla_oproj uses for S x D (host only)."""
+    lib = load()
+    tm, tn, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _raise(lib, lib.mla_oproj_plan(int(S), int(D), int(cus), ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(wg)))
+    return {"tile_m": tm.value, "tile_n": tn.value, "workgroups": wg.value}
+
+
+class PreparedOproj:
+    """A validated o_proj call whose arguments are marshalled once."""
+
+    def __init__(self, core, w_o, out):
+        self._lib = load()
+        _need(core.is_cuda, ValueError, "tensors must be on a GPU")
+        self._keep = (core, w_o, out)
+        self.args = _oproj_args(core, w_o, out)
+        self.device = core.device
+        _raise(self._lib, self._lib.mla_oproj_check(*self.args))
+
+    def __call__(self, stream: int | None = None):
+        s = _stream(self.device) if stream is None else stream
+        st = self._lib.mla_oproj(*self.args, ctypes.c_void_p(s))
+        if st:
+            _raise(self._lib, st)

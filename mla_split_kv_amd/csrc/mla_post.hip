@@ -42,9 +42,10 @@
 #include <string.h>
 
 #include <algorithm>
-#include <atomic>
 #include <string>
 
+#include "device.h"
+#include "launch.h"
 #include "mla_post.h"
 
 namespace {
@@ -1125,8 +1126,6 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_kernel(const uint8_t* x,
 
 // ---------------------------------------------------------------- host side
 
-thread_local std::string g_hip_error;
-
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow(a, b, out); }
 
@@ -1204,23 +1203,8 @@ int check_args(const mla_post_args* in) {
   return MLA_POST_OK;
 }
 
-// Compute units of the current device (256 on an MI355X), asked of the
-// runtime once per device; 256 if the runtime cannot tell.
-int device_cus() {
-  constexpr int MAX_DEVICES = 64;
-  static std::atomic<int> cached[MAX_DEVICES];  // 0: not asked yet
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  const bool slot = dev >= 0 && dev < MAX_DEVICES;
-  if (slot) {
-    const int c = cached[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (slot) cached[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
+using mla_dev::device_cus;
+using mla_dev::launch;
 
 // Workgroups per head of the persistent kernel (the grid is 12 times that).
 // `fill` is WG_PER_CU workgroups per CU in the grid, 2 of them resident (64
@@ -1264,30 +1248,6 @@ int workgroups_per_head(int S, int n, int cus) {
   if (ntiles <= fill) return fill;
   if (2 * ntiles <= 3 * fill && one_round > 0) return one_round;
   return fill;
-}
-
-int launched(hipError_t e) {
-  if (e != hipSuccess) {
-    g_hip_error = hipGetErrorString(e);
-    return MLA_POST_ELAUNCH;
-  }
-  return MLA_POST_OK;
-}
-
-template <class T>
-struct same_type {
-  using type = T;
-};
-
-// Enqueue kernel k and report this launch's own status: hipLaunchKernel
-// returns the error of this launch, so an error left pending by an earlier
-// HIP call (the caller's, or a device query) is neither taken for it nor
-// cleared. The arguments are converted to the kernel's parameter types
-// before their addresses are taken.
-template <typename... P>
-int launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t stream, typename same_type<P>::type... args) {
-  void* argv[] = {static_cast<void*>(&args)...};
-  return launched(hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, stream));
 }
 
 // Tokens per workgroup of the one-tile instance: 8 while that grid stays
@@ -1565,7 +1525,7 @@ const char* mla_post_strerror(int status) {
   }
 }
 
-const char* mla_post_last_hip_error(void) { return g_hip_error.c_str(); }
+const char* mla_post_last_hip_error(void) { return mla_dev::g_hip_error.c_str(); }
 
 int mla_post_version(void) { return MLA_POST_VERSION; }
 

@@ -158,3 +158,33 @@ def check_all(o, lse, w_codes, w_scales, gate, g, exact_t1: bool = False, strict
     tot["t4_rel_rms"] = rel
     tot["tokens"] = S
     return tot
+
+
+# ---------------------------------------------------------------- o_proj
+
+
+def check_t5(out_gpu, ref, K: int, min_exact: float = 0.9) -> dict:
+    """T5, o_proj: out = bf16(sum_k core[t, k] W_O[d, k]) with float32
+    accumulation. Every product of two bf16 values is exact in float32, so
+    in any order of float32 additions the sum's error is at most
+    g = gamma_K M, gamma_K = K u / (1 - K u), u = 2^-24, M = sum_k |core W_O|
+    (the standard bound for recursive summation); one rounding to bf16 adds
+    at most half a bf16 ulp of the float32 sum. The bound per element:
+    |out - y| <= g + ulp_bf16(|y| + g), y the exact sum. A NaN fails.
+    That bound is the worst case; a float32 sum is typically about sqrt(K)
+    times closer, so nearly every output is RNE(y) itself: at least
+    min_exact of them must be (a statistical check, which a wrong final
+    rounding, such as truncation, fails). Also reported: the largest error
+    in units of the bound."""
+    u = 2.0**-24
+    gam = K * u / (1 - K * u)
+    g = gam * ref["mag"]
+    y = ref["y"]
+    tol = g + O.ulp_bf16(np.abs(y) + g)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(O.bf16_to_f64(out_gpu) - y)
+        bad = ~(err <= tol)
+    assert not bad.any(), f"T5: {int(bad.sum())} o_proj outputs outside the float32 summation bound"
+    exact = float(np.mean(out_gpu == ref["out"])) if out_gpu.size else 1.0
+    assert exact >= min_exact, f"T5: only {exact:.3f} of the outputs are the exact sum's bf16 rounding"
+    return {"t5_exact_frac": exact, "t5_max_err_over_bound": float(np.max(err / tol)) if err.size else 0.0}

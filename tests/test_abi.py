@@ -16,15 +16,18 @@ import torch
 import mla_split_kv_amd as m
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_post.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 OK, EINVAL, ESTRIDE, EALIGN, ERANGE, EUNSUP = 0, -1, -2, -3, -4, -5
 
 
 def header_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", src, flags=re.M)))
+    """Every mla_* function the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -212,7 +215,7 @@ def test_token_count_limit(lib):
     assert check(lib, a) == OK
     a = good_args(n=2, S=(1 << 30) + 4)
     assert check(lib, a) == EINVAL
-    src = open(HEADER).read()
+    src = open(os.path.join(ROOT, "include", "mla_post.h")).read()
     assert "#define MLA_POST_SMAX (1 << 30)" in src
 
 

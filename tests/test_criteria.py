@@ -99,3 +99,38 @@ def test_t4_rejects_nonzero_core_in_empty_head(case):
     core[t, 128 * h + 7] = 0x0001  # the smallest subnormal: far inside 2e-2 RMS of the row
     with pytest.raises(AssertionError, match="T4"):
         C.check_t4(core, ref, ref["lat"], ref["codes"], ref["scales"])
+
+
+def test_t5_accepts_float32_sums_and_rejects_mistakes():
+    """T5 (o_proj): a float32 sum rounded to bf16 (numpy's float32 matrix
+    product, another summation order) passes; a NaN, an output missing its
+    largest product, a transposed result and a truncating final rounding
+    fail."""
+    from oracle.oproj import oproj
+
+    rng = np.random.default_rng(5)
+    S, D, K = 9, 40, 1536
+    core = synth.f32_to_bf16_bits(rng.standard_normal((S, K), dtype=np.float32))
+    w = synth.f32_to_bf16_bits(rng.standard_normal((D, K), dtype=np.float32) / np.float32(40))
+    ref = oproj(core, w)
+    a, b = O.bf16_to_f64(core), O.bf16_to_f64(w)
+    f32 = a.astype(np.float32) @ b.astype(np.float32).T
+    got = synth.f32_to_bf16_bits(f32)
+    C.check_t5(got, ref, K)
+    bad = got.copy()
+    bad[2, 3] = 0x7FC0
+    with pytest.raises(AssertionError, match="T5"):
+        C.check_t5(bad, ref, K)
+    bad = got.copy()
+    terms = a[4] * b[5]
+    kmax = int(np.argmax(np.abs(terms)))
+    bad[4, 5] = O.rne_bf16(ref["y"][4, 5] - terms[kmax])
+    with pytest.raises(AssertionError, match="T5"):
+        C.check_t5(bad, ref, K)
+    sq = oproj(core, w[:S])  # square S x S
+    t = synth.f32_to_bf16_bits((a.astype(np.float32) @ b[:S].astype(np.float32).T).T)
+    with pytest.raises(AssertionError, match="T5"):
+        C.check_t5(t, sq, K)
+    trunc = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    with pytest.raises(AssertionError, match="T5"):
+        C.check_t5(trunc, ref, K)

@@ -261,3 +261,18 @@ def test_device_plan_is_the_table(gpu_lib):
     launches there are the ones the table above pins."""
     for (n, S, lse), _ in TABLE:
         assert m.plan_args(args(n, S, lse), 0) == plan(n, S, lse)
+
+
+def test_oproj_plan_tiles():
+    """o_proj's tile at 256 CUs: 128 x 128 while that grid gives each CU two
+    workgroups (the large batch: 32 x 56 tiles), smaller tiles for small
+    batches; the grid covers S x D."""
+    import mla_split_kv_amd as m
+
+    p = m.oproj_plan(4096, 7168, 256)
+    assert (p["tile_m"], p["tile_n"], p["workgroups"]) == (128, 128, 32 * 56)
+    p = m.oproj_plan(64, 7168, 256)
+    assert (p["tile_m"], p["tile_n"]) == (64, 64) and p["workgroups"] == 112
+    for S, D in ((1, 8), (37, 136), (300, 1024), (4096, 7168), (5000, 264)):
+        p = m.oproj_plan(S, D, 256)
+        assert p["workgroups"] == -(-S // p["tile_m"]) * -(-D // p["tile_n"])
