@@ -725,6 +725,97 @@ def pin_oproj_known_answers():
     assert np.all(r3["out"][:, [0, 1, 2, 4, 5]] == 0)
 
 
+# ---------------------------------------------------------------- the split-KV attention (producer)
+
+
+def _attn_case(rng, lens, q, sigma_q=1.0):
+    import oracle.attention as A
+
+    R = len(lens)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    kv = bf16_bits_from_f32(rng.standard_normal((int(indptr[-1]), A.DQK)))
+    qry = bf16_bits_from_f32(rng.standard_normal((R * q, A.NH, A.DQK)) * sigma_q)
+    return qry, kv, indptr
+
+
+def pin_attention_split_equals_unsplit():
+    """Merging a request's split partials (float64, the merge's own
+    definition) gives its unsplit attention, for split counts that leave some
+    splits empty; the unsplit attention equals a scalar walk-through (scores,
+    softmax, weighted sum of the 512 value dims) written out with loops."""
+    import oracle.attention as A
+
+    rng = np.random.default_rng(50)
+    qry, kv, indptr = _attn_case(rng, [7, 0, 3, 20], q=2)
+    scale = 1.0 / np.sqrt(192.0)
+    one = A.attention_partials(qry, kv, indptr, 2, 1, scale)
+    for per in (2, 3, 5, 9):
+        sp = A.attention_partials(qry, kv, indptr, 2, per, scale)
+        R = indptr.size - 1
+        for r in range(R):
+            x, _ = O.merge_values(sp["o"][r], sp["lse"][r])  # [q, 12, 512]
+            ref = one["o"][r, 0]
+            assert np.all(np.abs(x - ref) <= 1e-12 * max(1.0, np.abs(ref).max())), (per, r)
+    # scalar walk-through for request 2 (3 rows), token 1, heads 0 and 7
+    qv, kvv = O.bf16_to_f64(qry), O.bf16_to_f64(kv)
+    for h in (0, 7):
+        t = 2 * 2 + 1
+        rows = range(int(indptr[2]), int(indptr[3]))
+        sc = [scale * sum(qv[t, h, d] * kvv[i, d] for d in range(A.DQK)) for i in rows]
+        mx = max(sc)
+        ws = [np.exp(v - mx) for v in sc]
+        out = [sum(ws[n] * kvv[i, d] for n, i in enumerate(rows)) / sum(ws) for d in range(A.KVL)]
+        assert np.allclose(one["o"][2, 0, 1, h], out, rtol=1e-12, atol=1e-12)
+        assert abs(one["lse"][2, 0, 1, h] - (mx + np.log(sum(ws)))) <= 1e-12
+
+
+def pin_attention_bounds_empty_single():
+    """Split bounds are floor(j L / per) (hand values); a split without rows
+    has LSE -inf and a zero partial; a split of one row returns that row's
+    latent part exactly, with its score as LSE."""
+    import oracle.attention as A
+
+    assert list(A.split_bounds(10, 4)) == [0, 2, 5, 7, 10]
+    assert list(A.split_bounds(3, 5)) == [0, 0, 1, 1, 2, 3]
+    assert list(A.split_bounds(0, 2)) == [0, 0, 0]
+    rng = np.random.default_rng(51)
+    qry, kv, indptr = _attn_case(rng, [3], q=1)
+    p = A.attention_partials(qry, kv, indptr, 1, 5, 0.1)
+    for j, n in enumerate(np.diff(A.split_bounds(3, 5))):
+        if n == 0:
+            assert np.all(p["lse"][0, j] == -np.inf) and np.all(p["o"][0, j] == 0)
+        else:
+            i = int(A.split_bounds(3, 5)[j])
+            assert np.array_equal(p["o_bits"][0, j, 0], np.broadcast_to(kv[i, : A.KVL], (A.NH, A.KVL)))
+            s = 0.1 * O.bf16_to_f64(qry)[0] @ O.bf16_to_f64(kv)[i]
+            assert np.allclose(p["lse"][0, j, 0], s, rtol=0, atol=1e-12)
+
+
+def pin_attention_rotary_dims_and_scale():
+    """The 64 rotary dims enter the scores but never the values: with the
+    query's rotary dims zero, changing the cache's rotary dims changes
+    nothing; with them set, it changes the LSEs. Doubling the scale equals
+    doubling the query."""
+    import oracle.attention as A
+
+    rng = np.random.default_rng(52)
+    qry, kv, indptr = _attn_case(rng, [6, 9], q=2)
+    q0 = qry.copy()
+    q0[..., A.KVL :] = 0
+    kv2 = kv.copy()
+    kv2[:, A.KVL :] = bf16_bits_from_f32(rng.standard_normal((kv.shape[0], A.DQK - A.KVL)) * 5)
+    a = A.attention_partials(q0, kv, indptr, 2, 2, 0.07)
+    b = A.attention_partials(q0, kv2, indptr, 2, 2, 0.07)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
+    c = A.attention_partials(qry, kv, indptr, 2, 2, 0.07)
+    d = A.attention_partials(qry, kv2, indptr, 2, 2, 0.07)
+    assert not np.allclose(c["lse"], d["lse"])
+    q2 = O.rne_bf16(2.0 * O.bf16_to_f64(qry))
+    e = A.attention_partials(q2, kv, indptr, 2, 2, 0.07)
+    f = A.attention_partials(qry, kv, indptr, 2, 2, 0.14)
+    assert np.allclose(e["o"], f["o"], rtol=1e-12, atol=1e-13) and np.allclose(e["lse"], f["lse"], rtol=1e-12)
+
+
 ALL_PINS = [
     pin_textbook_attention,
     pin_single_partial_identity,
@@ -750,4 +841,7 @@ ALL_PINS = [
     pin_push_mask,
     pin_oproj_exact_rational,
     pin_oproj_known_answers,
+    pin_attention_split_equals_unsplit,
+    pin_attention_bounds_empty_single,
+    pin_attention_rotary_dims_and_scale,
 ]

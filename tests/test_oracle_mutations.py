@@ -200,6 +200,57 @@ MUTATIONS = [
     ("ulp exponent off by one", "ulp_bf16", _ulp_exponent_off_by_one, [pins.pin_ulp_bf16_brute]),
 ]
 
+import oracle.attention as AT  # noqa: E402
+
+_orig_attn = AT.attention_partials
+_orig_bounds = AT.split_bounds
+
+
+def _attn_rope_values(qry_bits, kv_bits, indptr, q, per, scale):
+    kv = np.asarray(kv_bits).copy()
+    kv[:, : AT.KVL] = np.concatenate([kv[:, AT.DQK - AT.KVL :]], axis=1)  # values read from the last 512 dims
+    r = _orig_attn(qry_bits, kv_bits, indptr, q, per, scale)
+    r2 = _orig_attn(qry_bits, kv, indptr, q, per, scale)
+    r["o"], r["o_bits"] = r2["o"], r2["o_bits"]
+    return r
+
+
+def _attn_lse_base2(qry_bits, kv_bits, indptr, q, per, scale):
+    r = _orig_attn(qry_bits, kv_bits, indptr, q, per, scale)
+    r["lse"] = r["lse"] / np.log(2.0)
+    r["lse_f32"] = r["lse"].astype(np.float32)
+    return r
+
+
+def _bounds_ceil(L, per):
+    return np.array([-((-j * L) // per) for j in range(per + 1)], dtype=np.int64)
+
+
+def _attn_no_scale(qry_bits, kv_bits, indptr, q, per, scale):
+    return _orig_attn(qry_bits, kv_bits, indptr, q, per, 1.0)
+
+
+ATTN_MUTATIONS = [
+    ("values from the rotary end", "attention_partials", _attn_rope_values, [pins.pin_attention_rotary_dims_and_scale]),
+    ("LSE in base 2", "attention_partials", _attn_lse_base2, [pins.pin_attention_split_equals_unsplit]),
+    ("split bounds rounded up", "split_bounds", _bounds_ceil, [pins.pin_attention_bounds_empty_single]),
+    ("scale ignored", "attention_partials", _attn_no_scale, [pins.pin_attention_rotary_dims_and_scale]),
+]
+
+
+@pytest.mark.parametrize("name,attr,fn,catchers", ATTN_MUTATIONS, ids=[m[0] for m in ATTN_MUTATIONS])
+def test_attention_mutation_is_caught(monkeypatch, name, attr, fn, catchers):
+    monkeypatch.setattr(AT, attr, fn)
+    caught = []
+    for pin in catchers:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake '{name}' passed every pin in {[p.__name__ for p in catchers]}"
+
+
 OPROJ_MUTATIONS = [
     ("W_O read transposed", _oproj_w_transposed, [pins.pin_oproj_known_answers]),
     ("o_proj rounded by truncation", _oproj_truncated, [pins.pin_oproj_exact_rational]),
