@@ -75,6 +75,42 @@ class MlaPostArgs(ctypes.Structure):
 ARGS_V1_SIZE = 176  # MLA_POST_ARGS_V1_SIZE: the struct up to dbg_scales
 
 
+class MlaDecodeArgs(ctypes.Structure):
+    """Mirror of ``mla_decode_args`` in include/mla_decode.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("R", ctypes.c_int32),
+        ("q", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("qry", ctypes.c_void_p),
+        ("q_st", ctypes.c_int64),
+        ("q_sh", ctypes.c_int64),
+        ("kv", ctypes.c_void_p),
+        ("kv_st", ctypes.c_int64),
+        ("indptr", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("w_v", ctypes.c_void_p),
+        ("w_sh", ctypes.c_int64),
+        ("w_sv", ctypes.c_int64),
+        ("w_v_scale", ctypes.c_void_p),
+        ("s_sh", ctypes.c_int64),
+        ("s_sv", ctypes.c_int64),
+        ("s_sb", ctypes.c_int64),
+        ("gate", ctypes.c_void_p),
+        ("core", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_int64),
+        ("dbg_lat", ctypes.c_void_p),
+        ("dbg_codes", ctypes.c_void_p),
+        ("dbg_scales", ctypes.c_void_p),
+    ]
+
+
+DQK = 576  # MLA_DECODE_DQK
+
+
 class MlaPostPlan(ctypes.Structure):
     """mla_post_plan: the launch mla_post makes for a call."""
 
@@ -109,6 +145,11 @@ EXPORTS = (
     "mla_oproj",
     "mla_oproj_check",
     "mla_oproj_plan",
+    "mla_decode",
+    "mla_decode_partials",
+    "mla_decode_check",
+    "mla_decode_workspace",
+    "mla_decode_workspace_init",
 )
 
 _lib = None
@@ -159,6 +200,16 @@ def load() -> ctypes.CDLL:
     lib.mla_oproj_check.restype = ctypes.c_int
     lib.mla_oproj_plan.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.mla_oproj_plan.restype = ctypes.c_int
+    for f in ("mla_decode", "mla_decode_partials"):
+        getattr(lib, f).argtypes = [ctypes.POINTER(MlaDecodeArgs), vp]
+        getattr(lib, f).restype = ctypes.c_int
+    lib.mla_decode_check.argtypes = [ctypes.POINTER(MlaDecodeArgs)]
+    lib.mla_decode_check.restype = ctypes.c_int
+    pi64 = ctypes.POINTER(i64)
+    lib.mla_decode_workspace.argtypes = [i32, i32, i32, pi64, pi64, pi64, pi64]
+    lib.mla_decode_workspace.restype = ctypes.c_int
+    lib.mla_decode_workspace_init.argtypes = [vp, i32, vp]
+    lib.mla_decode_workspace_init.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -447,5 +498,133 @@ class PreparedOproj:
     def __call__(self, stream: int | None = None):
         s = _stream(self.device) if stream is None else stream
         st = self._lib.mla_oproj(*self.args, ctypes.c_void_p(s))
+        if st:
+            _raise(self._lib, st)
+
+
+# ---------------------------------------------------------------- split-KV attention fused with mla_post (include/mla_decode.h)
+
+
+def decode_workspace_layout(R: int, q: int, n: int) -> dict:
+    """Bytes and part offsets of mla_decode's workspace (host only)."""
+    lib = load()
+    b, c, p, l = (ctypes.c_int64() for _ in range(4))
+    _raise(lib, lib.mla_decode_workspace(int(R), int(q), int(n), ctypes.byref(b), ctypes.byref(c), ctypes.byref(p), ctypes.byref(l)))
+    return {"bytes": b.value, "counters": c.value, "partials": p.value, "lse": l.value}
+
+
+class DecodeWorkspace:
+    """A device workspace for mla_decode calls of R requests, q tokens, n
+    splits: a uint8 tensor of the library's size (allocated by torch, not by
+    the library), its counters zeroed once by mla_decode_workspace_init."""
+
+    def __init__(self, R: int, q: int, n: int, device="cuda"):
+        lib = load()
+        self.R, self.q, self.n = int(R), int(q), int(n)
+        self.layout = decode_workspace_layout(R, q, n)
+        self.buf = torch.empty(self.layout["bytes"] + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.mem = self.buf[off : off + self.layout["bytes"]]
+        _raise(lib, lib.mla_decode_workspace_init(ctypes.c_void_p(self.mem.data_ptr()), self.R, ctypes.c_void_p(_stream(self.mem.device))))
+
+    def counters(self):
+        c = self.layout["counters"]
+        return self.mem[c : c + 4 * self.R].view(torch.int32)
+
+    def partials(self):
+        """(o bf16 [R, n, q, 12, 512], lse float32 [R, n, q, 12]) views."""
+        p, l = self.layout["partials"], self.layout["lse"]
+        rows = self.R * self.n * self.q * NH
+        o = self.mem[p : p + rows * KVL * 2].view(torch.bfloat16).view(self.R, self.n, self.q, NH, KVL)
+        lse = self.mem[l : l + rows * 4].view(torch.float32).view(self.R, self.n, self.q, NH)
+        return o, lse
+
+    def token_views(self):
+        """The partials as mla_post takes them: o [n, S, 12, 512] and lse
+        [n, S, 12] strided views plus the request-major layout arguments."""
+        o, lse = self.partials()
+        S = self.R * self.q
+        so, sl = o.stride(), lse.stride()
+        ov = o.as_strided((self.n, S, NH, KVL), (so[1], so[2], so[3], 1), o.storage_offset())
+        lv = lse.as_strided((self.n, S, NH), (sl[1], sl[2], sl[3]), lse.storage_offset())
+        lay = {"q": self.q, "o_sr": so[0] - self.q * so[2], "l_sr": sl[0] - self.q * sl[2]}
+        return ov, lv, lay
+
+
+def _decode_args(qry, kv, indptr, q, n, scale, w_v, w_v_scale, gate, core, ws, dbg=None) -> MlaDecodeArgs:
+    _need(qry.dtype == torch.bfloat16 and qry.dim() == 3 and tuple(qry.shape[1:]) == (NH, DQK) and qry.stride(2) == 1,
+          TypeError, "qry must be bf16 [S, 12, 576] with unit innermost stride")
+    _need(kv.dtype == torch.bfloat16 and kv.dim() == 2 and kv.shape[1] == DQK and kv.stride(1) == 1, TypeError,
+          "kv must be bf16 [rows, 576] with unit innermost stride")
+    _need(indptr.dtype == torch.int32 and indptr.dim() == 1 and indptr.is_contiguous(), TypeError, "indptr must be int32 [R + 1]")
+    R = int(indptr.shape[0]) - 1
+    S = int(qry.shape[0])
+    _need(R >= 0 and S == R * q, ValueError, f"qry has {S} tokens, expected R * q = {R * q}")
+    _need((ws.R, ws.q, ws.n) == (R, q, n), ValueError, "workspace made for another (R, q, n)")
+    _need(w_v.dtype == torch.uint8 and tuple(w_v.shape) == (NH, VD, KVL // 2) and w_v.stride(-1) == 1, TypeError,
+          "w_v must be uint8 [12,128,256]")
+    _need(w_v_scale.dtype == torch.uint8 and tuple(w_v_scale.shape) == (NH, VD, KVL // 32), TypeError,
+          "w_v_scale must be uint8 [12,128,16]")
+    for name, t in (("gate", gate), ("core", core)):
+        _need(t.dtype == torch.bfloat16 and tuple(t.shape) == (S, GROWS) and t.is_contiguous(), ValueError,
+              f"{name} must be contiguous bf16 [{S}, 1536]")
+    a = MlaDecodeArgs()
+    a.struct_size = ctypes.sizeof(MlaDecodeArgs)
+    a.R, a.q, a.n = R, int(q), int(n)
+    a.qry, a.q_st, a.q_sh = qry.data_ptr(), qry.stride(0), qry.stride(1)
+    a.kv, a.kv_st = kv.data_ptr(), kv.stride(0)
+    a.indptr = indptr.data_ptr()
+    a.scale = float(scale)
+    a.w_v, a.w_sh, a.w_sv = w_v.data_ptr(), w_v.stride(0), w_v.stride(1)
+    a.w_v_scale = w_v_scale.data_ptr()
+    a.s_sh, a.s_sv, a.s_sb = w_v_scale.stride(0), w_v_scale.stride(1), w_v_scale.stride(2)
+    a.gate, a.core = gate.data_ptr(), core.data_ptr()
+    a.workspace, a.workspace_bytes = ws.mem.data_ptr(), ws.layout["bytes"]
+    if dbg is not None:
+        a.dbg_lat, a.dbg_codes, a.dbg_scales = (t.data_ptr() for t in dbg)
+    return a
+
+
+def mla_decode(qry, kv, indptr, q: int, n: int, scale: float, w_v, w_v_scale, gate, ws: DecodeWorkspace, core=None,
+               debug: bool = False, fused: bool = True):
+    """Split-KV MLA decode attention and mla_post on torch's current stream.
+
+    fused=True: one launch (include/mla_decode.h's mla_decode); returns core
+    (with debug=True: core, latents, codes, scales of the merge).
+    fused=False: the attention alone (mla_decode_partials); its partials are
+    left in ws (ws.partials(), ws.token_views()) and core is not written."""
+    lib = load()
+    S = int(qry.shape[0])
+    if core is None:
+        core = torch.empty((S, GROWS), dtype=torch.bfloat16, device=gate.device)
+    dbg = None
+    if debug:
+        dev = core.device
+        dbg = (torch.empty((S, NH, KVL), dtype=torch.bfloat16, device=dev),
+               torch.empty((S, NH, KVL // 2), dtype=torch.uint8, device=dev),
+               torch.empty((S, NH, KVL // 32), dtype=torch.uint8, device=dev))
+    a = _decode_args(qry, kv, indptr, q, n, scale, w_v, w_v_scale, gate, core, ws, dbg)
+    _need(core.is_cuda, ValueError, "tensors must be on a GPU")
+    f = lib.mla_decode if fused else lib.mla_decode_partials
+    _raise(lib, f(ctypes.byref(a), ctypes.c_void_p(_stream(core.device))))
+    return core if not debug else (core,) + dbg
+
+
+class PreparedDecode:
+    """A validated mla_decode call (fused or the attention alone) whose
+    argument struct is built once."""
+
+    def __init__(self, qry, kv, indptr, q, n, scale, w_v, w_v_scale, gate, ws, core, fused=True):
+        self._lib = load()
+        self._keep = (qry, kv, indptr, w_v, w_v_scale, gate, ws, core)
+        self.args = _decode_args(qry, kv, indptr, q, n, scale, w_v, w_v_scale, gate, core, ws)
+        self._ref = ctypes.byref(self.args)
+        self.device = core.device
+        self._f = self._lib.mla_decode if fused else self._lib.mla_decode_partials
+        _raise(self._lib, self._lib.mla_decode_check(self._ref))
+
+    def __call__(self, stream: int | None = None):
+        s = _stream(self.device) if stream is None else stream
+        st = self._f(self._ref, ctypes.c_void_p(s))
         if st:
             _raise(self._lib, st)

@@ -56,7 +56,10 @@ def attention_partials(qry_bits, kv_bits, indptr, q: int, per: int, scale: float
     qry_bits uint16 [S, 12, 576] bf16 (S = R q, token t of request t // q);
     kv_bits uint16 [rows, 576] bf16; indptr int [R + 1].
     Returns o (float64 [R, per, q, 12, 512]), lse (float64 [R, per, q, 12]),
-    o_bits (bf16 bits, A4) and lse_f32 (float32).
+    o_bits (bf16 bits, A4) and lse_f32 (float32); for tolerances also mag
+    (the softmax-weighted mean of |value|, per element of o) and smag
+    (scale times the largest sum over the dims of |q c| among the split's
+    rows, per (token, head): the size of the terms a score sums).
     """
     qv = bf16_to_f64(qry_bits)
     kv = bf16_to_f64(kv_bits)
@@ -65,6 +68,8 @@ def attention_partials(qry_bits, kv_bits, indptr, q: int, per: int, scale: float
     if qv.shape[0] != R * q:
         raise ValueError("S must be R * q")
     o = np.zeros((R, per, q, NH, KVL))
+    mag = np.zeros((R, per, q, NH, KVL))
+    smag = np.zeros((R, per, q, NH))
     lse = np.full((R, per, q, NH), -np.inf)
     for r in range(R):
         rows = kv[indptr[r] : indptr[r + 1]]
@@ -79,8 +84,10 @@ def attention_partials(qry_bits, kv_bits, indptr, q: int, per: int, scale: float
             p = np.exp(s - m)
             tot = p.sum(axis=-1)
             o[r, j] = np.einsum("thi,id->thd", p, c[:, :KVL]) / tot[..., None]
+            mag[r, j] = np.einsum("thi,id->thd", p, np.abs(c[:, :KVL])) / tot[..., None]
+            smag[r, j] = abs(scale) * np.einsum("thd,id->thi", np.abs(qr), np.abs(c)).max(axis=-1)
             lse[r, j] = m[..., 0] + np.log(tot)
-    return {"o": o, "lse": lse, "o_bits": rne_bf16(o), "lse_f32": lse.astype(np.float32)}
+    return {"o": o, "lse": lse, "o_bits": rne_bf16(o), "lse_f32": lse.astype(np.float32), "mag": mag, "smag": smag}
 
 
 def token_partials(parts):

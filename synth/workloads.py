@@ -311,6 +311,49 @@ def large_decode_request_major() -> Workload:
     )
 
 
+# ---- inputs of the split-KV decode attention that produces the partials ----
+
+DQK = 576  # query / cache row width: 512 latent + 64 rotary
+
+
+@dataclass
+class DecodeInputs:
+    """One fused decode call's inputs, host side: queries of R requests of q
+    tokens, the KV cache rows of every request back to back, W_V (bf16, to be
+    put into MXFP4 by the caller) and the gate."""
+
+    name: str
+    R: int
+    q: int
+    n: int  # KV splits per request
+    qry: np.ndarray  # uint16 [R q, 12, 576]
+    kv: np.ndarray  # uint16 [sum of lengths, 576]
+    indptr: np.ndarray  # int32 [R + 1]
+    wv_bits: np.ndarray  # uint16 [12, 128, 512]
+    gate: np.ndarray  # uint16 [R q, 1536]
+    scale: float
+
+    @property
+    def S(self) -> int:
+        return self.R * self.q
+
+
+def decode_inputs(name: str, lens, q: int, n: int, seed: int, q_sigma: float = 1.0, kv_sigma: float = 1.0,
+                  scale: float = 1.0 / np.sqrt(192.0)) -> DecodeInputs:
+    """Seeded draws: per-request KV lengths `lens`, queries ~ N(0, q_sigma)
+    and cache rows ~ N(0, kv_sigma) in bf16, W_V ~ N(0, 1/sqrt(512)), gate
+    ~ U(0, 1). Draw order: queries, cache, W_V, gate. The default scale is
+    1/sqrt(192), a DeepSeek-V3-style query-key head width of 128 + 64."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    R = lens.size
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    qry = _normal_bf16(rng, (R * q, NH, DQK), q_sigma)
+    kv = _normal_bf16(rng, (int(indptr[-1]), DQK), kv_sigma)
+    wv, gate = _wv_gate(rng, R * q)
+    return DecodeInputs(name, R, q, n, qry, kv, indptr, wv, gate, float(scale))
+
+
 STANDARD = {
     "tiny": tiny,
     "no_merge": no_merge,

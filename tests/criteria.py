@@ -188,3 +188,50 @@ def check_t5(out_gpu, ref, K: int, min_exact: float = 0.9) -> dict:
     exact = float(np.mean(out_gpu == ref["out"])) if out_gpu.size else 1.0
     assert exact >= min_exact, f"T5: only {exact:.3f} of the outputs are the exact sum's bf16 rounding"
     return {"t5_exact_frac": exact, "t5_max_err_over_bound": float(np.max(err / tol)) if err.size else 0.0}
+
+
+# ---------------------------------------------------------------- the split-KV attention (producer)
+
+
+def check_t0(o_gpu, lse_gpu, ref, nrows) -> dict:
+    """T0, the producer's partials against the float64 attention oracle.
+
+    o_gpu bf16 bits [R, n, q, 12, 512] and lse_gpu float32 [R, n, q, 12]
+    from the workspace; ref = oracle.attention.attention_partials; nrows
+    [R, n] the rows of each split. An empty split must give exactly +0
+    partials and an LSE of -inf. Otherwise, with rows the split's rows and
+    the score error e = (gamma_576 + 2^-22) smag (576 exact float32 products
+    summed in float32, then scaled; smag = scale max_i sum_d |q_d c_id|):
+      |lse_gpu - lse| <= 2 e + rows 2^-22 + 2^-20 (1 + |lse|)
+    (every score and the running maximum off by at most e; the float32 sum
+    of rows exponentials and the base-2 logarithm), and
+      |o_gpu - o| <= (2^-8 + 4 e + rows 2^-22) mag + ulp_bf16(|o|)
+    (each weight off by a relative 2e from the scores and 2^-9 from rounding
+    the probabilities to bf16 for the value product, the float32 sums, one
+    bf16 rounding; mag = the softmax-weighted mean of |value|). A NaN
+    fails."""
+    u = 2.0**-24
+    g576 = 576 * u / (1 - 576 * u)
+    e = (g576 + 2.0**-22) * ref["smag"]
+    rows = np.asarray(nrows, dtype=np.float64)[:, :, None, None]
+    empty = np.broadcast_to(rows == 0, ref["lse"].shape)
+    lg = np.asarray(lse_gpu, dtype=np.float64)
+    assert np.all(lg[empty] == -np.inf), "T0: an empty split's LSE is not -inf"
+    assert np.all(np.asarray(o_gpu)[empty] == 0), "T0: an empty split's partial is not +0"
+    live = ~empty
+    lr = ref["lse"]
+    with np.errstate(invalid="ignore"):
+        dl = np.abs(lg - lr)
+        tl = 2 * e + rows * 2.0**-22 + 2.0**-20 * (1 + np.abs(lr))
+        bad = live & ~(dl <= tl)
+    assert not bad.any(), f"T0: {int(bad.sum())} LSEs outside tolerance"
+    og = O.bf16_to_f64(o_gpu)
+    with np.errstate(invalid="ignore"):
+        do = np.abs(og - ref["o"])
+        to = (2.0**-8 + 4 * e[..., None] + rows[..., None] * 2.0**-22) * ref["mag"] + O.ulp_bf16(ref["o"])
+        bad = live[..., None] & ~(do <= to)
+    assert not bad.any(), f"T0: {int(bad.sum())} partial values outside tolerance"
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(live[..., None], do / np.maximum(to, 1e-300), 0)
+    return {"t0_partials": int(live.sum()), "t0_max_err_over_tol": float(rel.max()) if rel.size else 0.0,
+            "t0_exact_frac": float(np.mean((np.asarray(o_gpu) == ref["o_bits"])[np.broadcast_to(live[..., None], og.shape)])) if live.any() else 1.0}

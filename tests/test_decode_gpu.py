@@ -1,0 +1,148 @@
+"""The split-KV decode attention and its fusion with mla_post
+(include/mla_decode.h) on the GPU, through the C ABI, against the float64
+oracles (oracle/attention.py for the partials, oracle/post.py for the merge
+and W_UV).
+
+Each case checks:
+  T0     the partials and LSEs the attention leaves in the workspace against
+         the attention oracle (criteria.check_t0);
+  T1-T4  the fused launch's merge stage outputs and core against the
+         mla_post oracle run on those same partials;
+  the fused launch's core bit for bit against the unfused pair (the
+  attention alone, then mla_post on the workspace's partials in its
+  request-major layout), and the request counters back at zero.
+Inputs are seeded and synthetic (synth.decode_inputs).
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import criteria as C
+import oracle.attention as A
+import oracle.post as O
+import synth
+from gpu_support import bf16_to_dev, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def device_case(d, qry_pad=0, kv_pad=0):
+    """Device tensors of DecodeInputs d; queries and cache rows optionally as
+    views of wider buffers (row strides 576 + pad)."""
+    dev = "cuda"
+    if qry_pad:
+        wide = torch.zeros((d.S, 12, 576 + qry_pad), dtype=torch.bfloat16, device=dev)
+        wide[:, :, :576] = bf16_to_dev(d.qry, dev)
+        qry = wide[:, :, :576]
+    else:
+        qry = bf16_to_dev(d.qry, dev)
+    if kv_pad:
+        wide = torch.zeros((max(1, d.kv.shape[0]), 576 + kv_pad), dtype=torch.bfloat16, device=dev)
+        if d.kv.shape[0]:
+            wide[: d.kv.shape[0], :576] = bf16_to_dev(d.kv, dev)
+        kv = wide[: max(1, d.kv.shape[0]), :576]
+    else:
+        kv = bf16_to_dev(d.kv if d.kv.shape[0] else np.zeros((1, 576), np.uint16), dev)
+    wc, ws = O.quantize_mxfp4(d.wv_bits)
+    return {
+        "qry": qry,
+        "kv": kv,
+        "indptr": torch.from_numpy(d.indptr).to(dev),
+        "w_v": torch.from_numpy(wc).to(dev),
+        "w_s": torch.from_numpy(ws).to(dev),
+        "gate": bf16_to_dev(d.gate, dev),
+        "wc": wc,
+        "ws": ws,
+    }
+
+
+def check_case(m, d, **pads):
+    say(f"{d.name}: R={d.R} q={d.q} n={d.n} lens={np.diff(d.indptr).tolist()[:8]}.. pads={pads}")
+    t = device_case(d, **pads)
+    ws = m.DecodeWorkspace(d.R, d.q, d.n)
+    args = (t["qry"], t["kv"], t["indptr"], d.q, d.n, d.scale, t["w_v"], t["w_s"], t["gate"], ws)
+    core, lat, codes, scales = m.mla_decode(*args, debug=True)
+    torch.cuda.synchronize()
+    cnt = ws.counters().cpu().numpy()
+    assert np.all(cnt == 0), f"counters not reset: {cnt[cnt != 0][:8]}"
+    po, pl = ws.partials()
+    po_h, pl_h = to_bits(po), pl.cpu().numpy()
+    g = {"core": to_bits(core), "lat": to_bits(lat), "codes": codes.cpu().numpy(), "scales": scales.cpu().numpy()}
+    # the producer against the attention oracle
+    ref = A.attention_partials(d.qry, d.kv, d.indptr, d.q, d.n, d.scale)
+    lens = np.diff(d.indptr.astype(np.int64))
+    nrows = np.stack([np.diff(A.split_bounds(int(L), d.n)) for L in lens]) if d.R else np.zeros((0, d.n))
+    st = C.check_t0(po_h, pl_h, ref, nrows)
+    # the merge stage against the mla_post oracle on the GPU's own partials
+    o_tok = np.ascontiguousarray(np.transpose(po_h, (1, 0, 2, 3, 4)).reshape(d.n, d.S, 12, 512))
+    l_tok = np.ascontiguousarray(np.transpose(pl_h, (1, 0, 2, 3)).reshape(d.n, d.S, 12))
+    st.update(C.check_all(o_tok, l_tok, t["wc"], t["ws"], d.gate, g))
+    # the unfused pair gives the same core, bit for bit
+    ws2 = m.DecodeWorkspace(d.R, d.q, d.n)
+    m.mla_decode(*args[:-1], ws2, fused=False)
+    ov, lv, lay = ws2.token_views()
+    core2 = m.mla_post(ov, lv, t["w_v"], t["w_s"], t["gate"], **lay)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(ws2.partials()[0]), po_h), "the attention alone wrote other partials"
+    assert np.array_equal(to_bits(core2), g["core"]), "fused and unfused core differ"
+    # a second fused call on the same workspace: the same core
+    core3 = m.mla_decode(*args)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(core3), g["core"]), "a second call on the workspace differs"
+    say(f"{d.name}: {st}")
+    return st, g, ref
+
+
+CASES = [
+    # (name, lens, q, n, seed, options)
+    ("one_request", [200], 4, 3, 1, {}),
+    ("ragged_blocks", [1, 63, 64, 65, 129, 300, 0, 17], 4, 4, 2, {}),
+    ("empty_splits", [2, 5, 0, 3], 2, 6, 3, {}),  # L < n: some splits empty, one request empty
+    ("q1", [100, 37, 250], 1, 5, 4, {}),
+    ("q3", [77, 90, 16, 140, 5], 3, 2, 5, {}),
+    ("one_split", [130, 66], 4, 1, 6, {}),
+    ("many_splits", [700, 500], 4, 64, 7, {}),
+    ("R_not_multiple_of_8", [40] * 13, 4, 3, 8, {}),
+    ("strided", [90, 33, 160], 4, 3, 9, {"qry_pad": 64, "kv_pad": 32}),
+    ("wide_scores", [120, 64], 4, 2, 10, {"q_sigma": 4.0}),
+]
+
+
+@pytest.mark.parametrize("name,lens,q,n,seed,opts", CASES, ids=[c[0] for c in CASES])
+def test_decode(gpu_lib, name, lens, q, n, seed, opts):
+    opts = dict(opts)
+    pads = {k: opts.pop(k) for k in ("qry_pad", "kv_pad") if k in opts}
+    d = synth.decode_inputs(name, lens, q, n, seed, **opts)
+    st, g, _ = check_case(gpu_lib, d, **pads)
+    # a request without KV rows: its tokens' core rows are exactly +0
+    lens = np.asarray(lens)
+    for r in np.nonzero(lens == 0)[0]:
+        assert np.all(g["core"][r * q : (r + 1) * q] == 0)
+
+
+def test_decode_empty_batch_and_errors(gpu_lib):
+    m = gpu_lib
+    say("decode: R = 0 and argument errors")
+    ws = m.DecodeWorkspace(0, 4, 2)
+    qry = torch.zeros((0, 12, 576), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 576), dtype=torch.bfloat16, device="cuda")
+    indptr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    w_v = torch.zeros((12, 128, 256), dtype=torch.uint8, device="cuda")
+    w_s = torch.full((12, 128, 16), 127, dtype=torch.uint8, device="cuda")
+    gate = torch.zeros((0, 1536), dtype=torch.bfloat16, device="cuda")
+    core = m.mla_decode(qry, kv, indptr, 4, 2, 0.1, w_v, w_s, gate, ws)
+    torch.cuda.synchronize()
+    assert core.shape == (0, 1536)
+    with pytest.raises(m.MlaPostError):  # q past MLA_DECODE_QMAX
+        m.DecodeWorkspace(1, 5, 2)
+    with pytest.raises(m.MlaPostError):  # n past MLA_DECODE_NMAX
+        m.DecodeWorkspace(1, 4, 65)

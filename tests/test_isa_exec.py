@@ -6,10 +6,10 @@ store of a ragged tile) it would compute with stale operands. The kernels
 keep every MFMA ahead of lane-dependent control flow by construction (the
 result goes to an unconditional LDS store); this test compiles the device
 code to gfx950 assembly and checks the built code: no v_mfma lies inside a
-region where exec has been narrowed (s_and_saveexec / s_and exec ... up to
-the s_or exec that restores it; the compiler emits structured regions, so a
-linear scan tracks their nesting). The same scan must find narrowed regions
-around some stores, which shows that it sees them at all.
+region where exec may have been narrowed (s_and_saveexec / s_and exec ...
+up to the s_or exec that restores it, tracked over the control-flow graph of
+each kernel). The same scan must find narrowed regions around some stores,
+which shows that it sees them at all.
 """
 
 import os
@@ -20,27 +20,106 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc", "mla_post.hip")
+CSRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc")
+SRCS = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
-NARROW = re.compile(r"s_(and|andn2|or|xor)_saveexec_b64|s_(and|andn2|xor)_b64\s+exec,")
-RESTORE = re.compile(r"s_or_b64\s+exec,\s*exec")
+NARROW_SAVE = re.compile(r"s_(and|andn2|or|xor)_saveexec_b64\s+(s\[\d+:\d+\]|vcc)")
+NARROW_OP = re.compile(r"s_(and|andn2|xor)_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\]|vcc)")
+RESTORE = re.compile(r"s_or_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\])")
 
 
-def exec_depths(asm: str):
-    """(function, mnemonic, depth) for every MFMA and vector store."""
-    fn, depth, out = None, 0, []
+def functions(asm: str) -> dict:
+    """Kernel name -> its instruction and label lines."""
+    fn, out = None, {}
     for line in asm.splitlines():
         l = line.strip()
         m = re.match(r"^(_Z[_A-Za-z0-9]+):", l)
         if m:
-            fn, depth = m.group(1), 0
+            fn = m.group(1)
+            out[fn] = []
             continue
-        if NARROW.match(l):
-            depth += 1
-        elif RESTORE.match(l):
-            depth = max(0, depth - 1)
-        if l.startswith("v_mfma") or re.match(r"(global|buffer)_store", l):
-            out.append((fn, l.split()[0], depth))
+        if fn is None:
+            continue
+        if l.startswith(".Lfunc_end"):
+            fn = None
+            continue
+        out[fn].append(l)
+    return out
+
+
+def basic_blocks(lines):
+    """Basic blocks (label, instructions, successors) in layout order."""
+    bl, cur = [], {"label": None, "ins": []}
+    for l in lines:
+        m = re.match(r"^(\.LBB\d+_\d+):", l)
+        if m:
+            bl.append(cur)
+            cur = {"label": m.group(1), "ins": []}
+            continue
+        if not l or l.startswith(";") or l.startswith("."):
+            continue
+        cur["ins"].append(l)
+        if re.match(r"s_(branch|cbranch_\w+|endpgm|setpc_b64)\b", l):
+            bl.append(cur)
+            cur = {"label": None, "ins": []}
+    bl.append(cur)
+    bl = [b for b in bl if b["ins"] or b["label"]]
+    idx = {b["label"]: i for i, b in enumerate(bl) if b["label"]}
+    for i, b in enumerate(bl):
+        last = b["ins"][-1] if b["ins"] else ""
+        succ = []
+        m = re.match(r"s_branch\s+(\.LBB\d+_\d+)", last)
+        if m:
+            succ = [idx[m.group(1)]]
+        elif not re.match(r"s_(endpgm|setpc_b64)", last):
+            m = re.match(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)", last)
+            if m:
+                succ.append(idx[m.group(1)])
+            if i + 1 < len(bl):
+                succ.append(i + 1)
+        b["succ"] = succ
+    return bl
+
+
+def step(st: tuple, l: str) -> tuple:
+    """The stack of exec narrowings after instruction l: a saveexec or an
+    and/andn2/xor of exec pushes the register it uses; the s_or of exec with a
+    saved register pops back to that register's entry."""
+    m = NARROW_SAVE.match(l) or NARROW_OP.match(l)
+    if m:
+        return st + (m.group(2),)
+    m = RESTORE.match(l)
+    if m and m.group(1) in st:
+        k = max(j for j, r in enumerate(st) if r == m.group(1))
+        return st[:k]
+    return st
+
+
+def exec_depths(asm: str):
+    """(function, mnemonic, depth) for every MFMA and vector store: depth is
+    the number of exec narrowings that may be in force there, from a
+    dataflow over the kernel's control-flow graph (at a join the deeper
+    stack is kept, so the answer is conservative)."""
+    out = []
+    for fn, lines in functions(asm).items():
+        bl = basic_blocks(lines)
+        state, work = {0: ()}, [0]
+        while work:
+            i = work.pop()
+            st = state[i]
+            for l in bl[i]["ins"]:
+                st = step(st, l)
+            for s in bl[i]["succ"]:
+                old = state.get(s)
+                if old is None or (len(st) > len(old) and len(st) <= 16):
+                    state[s] = st
+                    work.append(s)
+        for i, b in enumerate(bl):
+            st = state.get(i, ())
+            for l in b["ins"]:
+                st = step(st, l)
+                if l.startswith("v_mfma") or re.match(r"(global|buffer)_store", l):
+                    out.append((fn, l.split()[0], len(st)))
     return out
 
 
@@ -57,10 +136,12 @@ def device_asm(src: str, tmp_path) -> str:
 
 
 @pytest.mark.slow
-def test_mfma_under_full_exec(tmp_path):
-    rows = exec_depths(device_asm(SRC, tmp_path))
+@pytest.mark.parametrize("src", SRCS, ids=os.path.basename)
+def test_mfma_under_full_exec(tmp_path, src):
+    rows = exec_depths(device_asm(src, tmp_path))
     mfma = [x for x in rows if x[1].startswith("v_mfma")]
     assert len(mfma) > 0, "no MFMA found in the device code"
     masked = [x for x in mfma if x[2] > 0]
     assert not masked, f"MFMAs under a narrowed exec mask: {masked[:5]}"
+    # the same scan sees the lane-conditional stores, so it does see narrowing
     assert any(d > 0 for _, m, d in rows if "store" in m), "the scan found no narrowed region at all"
