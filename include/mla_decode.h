@@ -112,6 +112,27 @@ int mla_decode_partials(const mla_decode_args* a, void* stream);
 /* The validation of mla_decode alone: host only, touches no device memory. */
 int mla_decode_check(const mla_decode_args* a);
 
+/* Size of the library's own device scratch array for mla_decode_noalloc. */
+#define MLA_DECODE_SCRATCH_BYTES (64ll << 20)
+
+/*
+ * mla_decode without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). The workspace is a
+ * file-scope device array of MLA_DECODE_SCRATCH_BYTES (64 MiB) that every GPU
+ * the library runs on holds until the process ends; its address is asked of
+ * the runtime once per device. a->workspace must be NULL (workspace_bytes is
+ * ignored). Calls whose workspace (mla_decode_workspace) exceeds the array
+ * return MLA_POST_EUNSUPPORTED and launch nothing. Each call first clears the
+ * array's counters with a small fill kernel on `stream`, then makes the fused
+ * launch; the partials and LSEs stay in the array until the next call. All
+ * calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads) race, and must be ordered by the caller.
+ * Calls no hipMalloc, hipFree or allocating routine. Same results as
+ * mla_decode with a workspace, bit for bit.
+ */
+int mla_decode_noalloc(const mla_decode_args* a, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -150,6 +150,7 @@ EXPORTS = (
     "mla_decode_check",
     "mla_decode_workspace",
     "mla_decode_workspace_init",
+    "mla_decode_noalloc",
 )
 
 _lib = None
@@ -210,6 +211,8 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_workspace.restype = ctypes.c_int
     lib.mla_decode_workspace_init.argtypes = [vp, i32, vp]
     lib.mla_decode_workspace_init.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [ctypes.POINTER(MlaDecodeArgs), vp]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -608,6 +611,33 @@ def mla_decode(qry, kv, indptr, q: int, n: int, scale: float, w_v, w_v_scale, ga
     f = lib.mla_decode if fused else lib.mla_decode_partials
     _raise(lib, f(ctypes.byref(a), ctypes.c_void_p(_stream(core.device))))
     return core if not debug else (core,) + dbg
+
+
+DECODE_SCRATCH_BYTES = 64 << 20  # MLA_DECODE_SCRATCH_BYTES
+
+
+class _NoWorkspace:
+    """Stands in for a DecodeWorkspace in mla_decode_noalloc's arguments."""
+
+    def __init__(self, R, q, n):
+        self.R, self.q, self.n = R, q, n
+        self.layout = {"bytes": 0}
+        self.mem = type("_Null", (), {"data_ptr": staticmethod(lambda: 0)})()
+
+
+def mla_decode_noalloc(qry, kv, indptr, q: int, n: int, scale: float, w_v, w_v_scale, gate, core=None):
+    """The fused launch with the library's own scratch array as workspace
+    (include/mla_decode.h's mla_decode_noalloc): nothing is allocated by the
+    library; returns core (allocated here by torch when not given)."""
+    lib = load()
+    S = int(qry.shape[0])
+    if core is None:
+        core = torch.empty((S, GROWS), dtype=torch.bfloat16, device=gate.device)
+    R = int(indptr.shape[0]) - 1
+    a = _decode_args(qry, kv, indptr, q, n, scale, w_v, w_v_scale, gate, core, _NoWorkspace(R, q, n))
+    _need(core.is_cuda, ValueError, "tensors must be on a GPU")
+    _raise(lib, lib.mla_decode_noalloc(ctypes.byref(a), ctypes.c_void_p(_stream(core.device))))
+    return core
 
 
 class PreparedDecode:

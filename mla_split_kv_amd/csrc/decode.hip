@@ -41,6 +41,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 #include "mla_decode.h"
@@ -503,6 +505,13 @@ __global__ void zero_counters(int32_t* c, int n) {
   if (i < n) c[i] = 0;
 }
 
+// The workspace of mla_decode_noalloc: a file-scope device array that every
+// GPU the library runs on holds until the process ends. In host code its name
+// is not a device address; its address on the current device comes from
+// hipGetSymbolAddress, asked once per device (scratch_on_device).
+constexpr int64_t SCRATCH_BYTES = MLA_DECODE_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
 // ---------------------------------------------------------------- host side
 
 bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
@@ -585,6 +594,28 @@ DArgs device_args(const mla_decode_args* a) {
   return d;
 }
 
+// scratch's address on the current device, or nullptr (with the HIP error
+// recorded) when the runtime cannot give it. Cached per device.
+void* scratch_on_device() {
+  constexpr int MAX_DEVICES = 64;
+  static std::atomic<void*> cached[MAX_DEVICES];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    mla_dev::g_hip_error = e != hipSuccess ? hipGetErrorString(e) : "device index out of range";
+    return nullptr;
+  }
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    mla_dev::g_hip_error = hipGetErrorString(e);
+    return nullptr;
+  }
+  cached[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 template <bool FUSED>
 int run(const mla_decode_args* a, void* stream) {
   const int st = check(a);
@@ -625,5 +656,33 @@ int mla_decode(const mla_decode_args* a, void* stream) { return run<true>(a, str
 int mla_decode_partials(const mla_decode_args* a, void* stream) { return run<false>(a, stream); }
 
 int mla_decode_check(const mla_decode_args* a) { return check(a); }
+
+int mla_decode_noalloc(const mla_decode_args* a, void* stream) {
+  if (!a || a->struct_size < sizeof(mla_decode_args)) return MLA_POST_EINVAL;
+  if (a->workspace) return MLA_POST_EINVAL;  // the workspace is the library's scratch array
+  if (a->R < 0 || a->R > (1 << 24) || a->q < 1 || a->q > MLA_DECODE_QMAX || a->n < 1) return MLA_POST_EINVAL;
+  if (a->n > MLA_DECODE_NMAX) return MLA_POST_EUNSUPPORTED;
+  WsLayout w;
+  ws_layout(a->R, a->q, a->n, &w);
+  if (w.bytes > SCRATCH_BYTES) return MLA_POST_EUNSUPPORTED;
+  if (a->R == 0) return check(a);
+  mla_decode_args b = *a;
+  b.struct_size = sizeof(mla_decode_args);
+  b.workspace = reinterpret_cast<void*>(256);  // stand-in for validation only (non-null, aligned)
+  b.workspace_bytes = SCRATCH_BYTES;
+  const int st = check(&b);
+  if (st != MLA_POST_OK) return st;
+  void* p = scratch_on_device();
+  if (!p) return MLA_POST_ELAUNCH;
+  b.workspace = p;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the counters must start at zero: a fill kernel (no memset, so the call
+  // may be captured in a graph)
+  const int z = launch(zero_counters, dim3((unsigned)((a->R + 255) / 256)), dim3(256), s, static_cast<int32_t*>(p), (int)a->R);
+  if (z != MLA_POST_OK) return z;
+  const DArgs d = device_args(&b);
+  const int64_t grid = (int64_t)XCDS * b.n * ((b.R + XCDS - 1) / XCDS);
+  return launch(mla_decode_kernel<true>, dim3((unsigned)grid), dim3(DTHREADS), s, d);
+}
 
 }  // extern "C"
