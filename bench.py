@@ -395,6 +395,71 @@ def oproj_bench(core, D: int, steps: int, warmup: int, m, torch) -> dict:
     }
 
 
+def read_ceiling(buf, steps: int, torch, m) -> dict:
+    """The plain-read reference (include/mla_measure.h): one streaming read of
+    the same partial buffer the fused kernel reads, 16-byte non-temporal loads
+    from every CU, timed like the kernel."""
+    sink = torch.empty(16, dtype=torch.uint8, device=buf.device)
+    t = time_gpu(lambda: m.measure_read(buf, sink), steps, 5, torch)
+    us = 1e3 * t["event_ms"] / steps
+    n = buf.numel() * buf.element_size()
+    return {"us": round(us, 3), "GBps": round(n / (us * 1e-6) / 1e9, 1), "bytes": n}
+
+
+def decode_bench(R: int, q: int, n: int, L: int, steps: int, warmup: int, m, torch) -> dict:
+    """The split-KV decode attention fused with mla_post (include/mla_decode.h)
+    at the large decode batch's sizes: R requests of q tokens, n splits, L
+    cache rows per request; queries and cache rows ~ N(0, 1) bf16, W_V ~
+    N(0, 1/sqrt(512)) into MXFP4 by the library's quantiser, gate ~ U(0, 1),
+    drawn on the device from a seeded generator. Times the fused launch, the
+    attention alone, mla_post on its partials, and that unfused pair."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    S = R * q
+    qry = torch.randn((S, 12, 576), generator=g, device="cuda").to(torch.bfloat16)
+    kv = torch.randn((R * L, 576), generator=g, device="cuda").to(torch.bfloat16)
+    indptr = torch.arange(R + 1, device="cuda", dtype=torch.int32) * L
+    wv = (torch.randn((12 * 128, 512), generator=g, device="cuda") / 512**0.5).to(torch.bfloat16)
+    codes, scales = m.quantize_mxfp4(wv)
+    w_v, w_s = codes.view(12, 128, 256), scales.view(12, 128, 16)
+    gate = torch.rand((S, 1536), generator=g, device="cuda").to(torch.bfloat16)
+    core = torch.empty((S, 1536), dtype=torch.bfloat16, device="cuda")
+    core2 = torch.empty_like(core)
+    ws = m.DecodeWorkspace(R, q, n)
+    scale = 1.0 / 192**0.5
+    fused = m.PreparedDecode(qry, kv, indptr, q, n, scale, w_v, w_s, gate, ws, core, fused=True)
+    attn = m.PreparedDecode(qry, kv, indptr, q, n, scale, w_v, w_s, gate, ws, core, fused=False)
+    ov, lv, lay = ws.token_views()
+    post = m.prepare(ov, lv, w_v, w_s, gate, core2, **lay)
+
+    def pair():
+        attn()
+        post()
+
+    res = {}
+    for name, call in (("fused", fused), ("attention", attn), ("mla_post", post), ("pair", pair)):
+        t = time_gpu(call, steps, warmup, torch)
+        res[name] = 1e3 * t["event_ms"] / steps
+    torch.cuda.synchronize()
+    same = bool(torch.equal(core, core2))
+    alg = R * L * 1152 + S * 12 * 576 * 2 + W_V_BYTES + 2 * S * 1536 * 2
+    gbps = alg / (res["fused"] * 1e-6) / 1e9
+    out = {
+        "workload": f"{R} requests x {q} tokens, {n} KV splits, {L} cache rows of 576 bf16 per request, 12 heads",
+        "us_fused": round(res["fused"], 1),
+        "us_attention_alone": round(res["attention"], 1),
+        "us_mla_post_on_partials": round(res["mla_post"], 1),
+        "us_unfused_pair": round(res["pair"], 1),
+        "fused_vs_pair": round(res["pair"] / res["fused"], 3),
+        "tokens_per_s_fused": round(S / (res["fused"] * 1e-6), 1),
+        "alg_bytes": alg,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "core_fused_equals_pair": same,
+    }
+    del qry, kv, ws
+    return out
+
+
 def calibrate_copy(torch) -> None:
     """A plain device-to-device copy of 1 GiB (torch dispatches it to the HIP
     runtime copy kernel __amd_rocclr_copyBuffer): counter
@@ -426,6 +491,8 @@ def main() -> int:
         "--cpu-workers", type=int, default=0, help="processes for the all-cores oracle timing (default min(16, CPUs); 1 skips it)"
     )
     ap.add_argument("--all", action="store_true", help="also time the four other standard workloads (stderr)")
+    ap.add_argument("--decode-kv-len", type=int, default=4096,
+                    help="also time the fused split-KV decode with this many cache rows per request (0: skip)")
     ap.add_argument("--oproj-d", type=int, default=7168,
                     help="also time o_proj on the call's core with this output width (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -497,6 +564,8 @@ def main() -> int:
     tokens_per_s = w.S * args.steps / t["wall_s"]
 
     copy_gbps = copy_ceiling(torch)
+    rc = read_ceiling(d["o_buf"], args.steps, torch, m)
+    log(f"plain read of the partial buffer: {rc}")
     op = None
     if args.oproj_d > 0:
         log(f"timing o_proj on the call's core, D = {args.oproj_d}")
@@ -588,9 +657,24 @@ def main() -> int:
             "frac": round(achieved / copy_gbps, 4),
             "what": "plain 1 GiB device copy, bytes read + written per second",
         },
+        "read_ceiling": {
+            "GBps": rc["GBps"],
+            "us": rc["us"],
+            "frac": round(rc["us"] / kernel_us, 4),
+            "what": "one streaming read of the same 805 MB partial buffer (mla_measure_read: 16-byte "
+            "non-temporal loads, a contiguous chunk per workgroup), timed like the kernel; frac is its "
+            "time over the kernel's",
+        },
     }
     if op:
         out["oproj"] = op
+    dec = None
+    if args.decode_kv_len > 0:
+        del d, call
+        log(f"timing the fused decode (1024 x 4 tokens, 16 splits, {args.decode_kv_len} rows per request)")
+        dec = decode_bench(1024, 4, 16, args.decode_kv_len, max(5, args.steps // 10), min(3, args.warmup), m, torch)
+        log(f"fused decode: {dec}")
+        out["fused_decode"] = dec
     if cpu_all:
         out["cpu_baseline_all_cores"] = cpu_all
     if extra:

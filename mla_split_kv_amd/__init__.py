@@ -151,6 +151,7 @@ EXPORTS = (
     "mla_decode_workspace",
     "mla_decode_workspace_init",
     "mla_decode_noalloc",
+    "mla_measure_read",
 )
 
 _lib = None
@@ -213,6 +214,8 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_workspace_init.restype = ctypes.c_int
     lib.mla_decode_noalloc.argtypes = [ctypes.POINTER(MlaDecodeArgs), vp]
     lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_measure_read.argtypes = [vp, i64, vp, vp]
+    lib.mla_measure_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -658,3 +661,18 @@ class PreparedDecode:
         st = self._f(self._ref, ctypes.c_void_p(s))
         if st:
             _raise(self._lib, st)
+
+
+# ---------------------------------------------------------------- bandwidth reference (include/mla_measure.h)
+
+
+def measure_read(t, sink=None):
+    """Read tensor t's bytes once (include/mla_measure.h's mla_measure_read) on
+    torch's current stream: the plain-read reference of the benchmark."""
+    lib = load()
+    _need(t.is_cuda and t.is_contiguous(), ValueError, "t must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.empty(16, dtype=torch.uint8, device=t.device)
+    n = t.numel() * t.element_size()
+    _raise(lib, lib.mla_measure_read(ctypes.c_void_p(t.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(_stream(t.device))))

@@ -3,7 +3,7 @@
     python -m mla_split_kv_amd.build
 
 Compiles every time it is called (the C-ABI library, its kernels and host code
-from csrc/mla_post.hip, csrc/oproj.hip and csrc/decode.hip). Packed-FP32 instructions are disabled for the device
+from csrc/mla_post.hip, oproj.hip, decode.hip and measure.hip). Packed-FP32 instructions are disabled for the device
 code; hipcc's host pass warns that it does not know that feature, harmlessly.
 build_c_client compiles tests/c/c_client.c, a plain C program that calls the
 library through the HIP runtime's C API, with gcc against include/ alone.
@@ -18,7 +18,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("mla_post.hip", "oproj.hip", "decode.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("mla_post.hip", "oproj.hip", "decode.hip", "measure.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_post.so")
 ARCH = "gfx950"

@@ -21,7 +21,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc")
-SRCS = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+# the sources with MFMAs: their own, or the shared helpers' (post_common.h)
+SRCS = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+              if f.endswith(".hip") and any(k in open(os.path.join(CSRC, f)).read()
+                                            for k in ("__builtin_amdgcn_mfma", '#include "post_common.h"')))
 
 NARROW_SAVE = re.compile(r"s_(and|andn2|or|xor)_saveexec_b64\s+(s\[\d+:\d+\]|vcc)")
 NARROW_OP = re.compile(r"s_(and|andn2|xor)_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\]|vcc)")
