@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MLA_POST_VERSION 3
+#define MLA_POST_VERSION 4
 
 /* Fixed shapes (the page's per-rank Kimi-K3 shapes at 8-way tensor parallelism). */
 #define MLA_POST_HEADS 12   /* local heads */
@@ -145,19 +145,25 @@ int mla_post_check(const mla_post_args* a);
 #define MLA_POST_KERNEL_PERSISTENT 2 /* workgroups that each keep one head and walk its tiles */
 #define MLA_POST_KERNEL_SPLIT_ROWS 3 /* one small token tile per workgroup, 8 / tile_tokens waves sharing the
                                         partials of each token (many partials, few tokens) */
+#define MLA_POST_KERNEL_STREAM 4     /* since version 4: workgroups that each keep one head and walk its tiles,
+                                        loading two tiles ahead straight into LDS (one or two partials, many
+                                        tokens) */
 
 typedef struct mla_post_plan {
   int32_t kernel;              /* MLA_POST_KERNEL_* */
-  int32_t tile_tokens;         /* tokens of a full tile: 8 or 16 (split-rows kernel: 1, 2 or 4) */
+  int32_t tile_tokens;         /* tokens of a full tile: 8 or 16 (split-rows kernel: 1, 2 or 4; streaming
+                                  kernel: 16 / n) */
   int32_t rows_held;           /* one-tile kernel: partial rows per token held at once (1, 2, 4, 8 or 16);
-                                  split-rows kernel: rows each wave holds at once (8 or 16); else 0 */
+                                  split-rows kernel: rows each wave holds at once (8 or 16); streaming
+                                  kernel: n; else 0 */
   int32_t lse_chunks;          /* persistent and split-rows kernels: 64-lane chunks of partials per token
                                   (1, 2, 4 or 8); else 1 */
   int32_t workgroups_per_head; /* the grid is 12 times this */
   int32_t workgroups;          /* grid size (workgroups of 512 threads) */
-  int32_t full_tiles;          /* persistent kernel: full 16-token tiles of every workgroup */
-  int32_t short_tokens;        /* persistent kernel: tokens of one more, shorter tile per workgroup (at most
-                                  16; the last workgroups of a head may get fewer or none); 0: none */
+  int32_t full_tiles;          /* persistent and streaming kernels: full tiles of every workgroup */
+  int32_t short_tokens;        /* persistent and streaming kernels: tokens of one more, shorter tile per
+                                  workgroup (at most tile_tokens; the last workgroups of a head may get
+                                  fewer or none); 0: none */
   int32_t pair_rows;           /* persistent kernel: rows of each of a wave's two tokens issued a tile ahead
                                   (4, for n <= 4 with LSEs); 0: 8 rows of its first token only */
   int32_t cus;                 /* compute units the plan was made for */

@@ -131,7 +131,7 @@ class MlaPostPlan(ctypes.Structure):
     ]
 
 
-KERNELS = {0: "none", 1: "one_tile", 2: "persistent", 3: "split_rows"}  # MLA_POST_KERNEL_*
+KERNELS = {0: "none", 1: "one_tile", 2: "persistent", 3: "split_rows", 4: "stream"}  # MLA_POST_KERNEL_*
 
 
 EXPORTS = (

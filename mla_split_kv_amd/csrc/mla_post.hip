@@ -243,6 +243,15 @@ __device__ __forceinline__ float lse_one(const KArgs& a, int t, int h) {
   return a.lse[(int64_t)(tc / a.q) * a.l_sr + (int64_t)tc * a.l_st + (int64_t)h * a.l_sh];
 }
 
+// Two bf16 values in one word with -0 made +0, the rest unchanged: a half's
+// sign bit is kept only where its magnitude bits are not all zero (adding
+// 0x7FFF to a magnitude of at most 0x7FFF sets bit 15 exactly when the
+// magnitude is nonzero, and never carries into the other half).
+__device__ __forceinline__ uint32_t plus_zero2(uint32_t w) {
+  const uint32_t m = w & 0x7FFF7FFFu;
+  return m | ((m + 0x7FFF7FFFu) & w & 0x80008000u);
+}
+
 // One partial: token t's row (tile slot tt, already loaded: v) is its
 // latents, unless its request is masked as having no KV, the token lies
 // past the batch (`empty`) or, with an LSE, that LSE sanitises to -inf.
@@ -258,11 +267,7 @@ __device__ __forceinline__ void copy_stage(const KArgs& a, int t, int tt, int h,
     lat[0] = v.x; lat[1] = v.y; lat[2] = v.z; lat[3] = v.w;
     if (a.lse) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = (lat[k] & 0x7FFFu) ? (lat[k] & 0xFFFFu) : 0u;
-        const uint32_t hi = (lat[k] & 0x7FFF0000u) ? (lat[k] & 0xFFFF0000u) : 0u;
-        lat[k] = hi | lo;
-      }
+      for (int k = 0; k < 4; ++k) lat[k] = plus_zero2(lat[k]);
     }
   }
   quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
@@ -434,34 +439,38 @@ struct TileSched {
   int count;  // tiles of this slot
 };
 
-// Full tiles per slot and the short tile's token count (host and device).
+// Full tiles per slot and the short tile's token count (host and device),
+// for tiles of TT tokens.
+template <int TT = TILE_T>
 __host__ __device__ inline void tile_counts(int S, int k, bool spread, int& main, int& chunk) {
-  main = S / (TILE_T * k);
-  const int rest = S - main * TILE_T * k;
-  chunk = spread ? (rest + k - 1) / k : (rest < TILE_T ? rest : TILE_T);
+  main = S / (TT * k);
+  const int rest = S - main * TT * k;
+  chunk = spread ? (rest + k - 1) / k : (rest < TT ? rest : TT);
 }
 
 // Whether leftover tokens are dealt out evenly (see TileSched): for one
 // partial (copied) and from SPREAD_MIN_N partials.
 __host__ __device__ inline bool spread_leftover(bool copy, int n) { return copy || n >= SPREAD_MIN_N; }
 
+template <int TT = TILE_T>
 __device__ __forceinline__ TileSched tile_sched(int S, int k, int slot, bool spread) {
   TileSched t;
   t.S = S;
   t.k = k;
   t.slot = slot;
-  tile_counts(S, k, spread, t.main, t.chunk);
-  t.base = t.main * TILE_T * k;
+  tile_counts<TT>(S, k, spread, t.main, t.chunk);
+  t.base = t.main * TT * k;
   t.count = t.main + (t.base + slot * t.chunk < S ? 1 : 0);
   return t;
 }
 
 // Tokens [t0, tend) of tile i of the slot; t0 = tend = S for an i past its
 // tiles.
+template <int TT = TILE_T>
 __device__ __forceinline__ void tile_span(const TileSched& t, int i, int& t0, int& tend) {
   if (i < t.main) {
-    t0 = (t.slot + i * t.k) * TILE_T;
-    tend = t0 + TILE_T;
+    t0 = (t.slot + i * t.k) * TT;
+    tend = t0 + TT;
   } else if (i < t.count) {
     t0 = t.base + t.slot * t.chunk;
     tend = min(t0 + t.chunk, t.S);
@@ -948,6 +957,329 @@ __global__ __launch_bounds__(THREADS) void mla_post_split_kernel(const KArgs a) 
   tile_wuv_store(a, wave, tl, kb, wv, sa, s_codes, s_scales, s_out, out);
 }
 
+// ---------------------------------------------------------------- the streaming kernel
+
+// One or two partials per (token, head) over many tokens. A 16-token tile
+// then reads only 16 KiB of rows; the persistent kernel keeps one tile's rows
+// in flight in registers and loads each tile's gate as it goes, so it waits
+// about one memory round trip per tile and spends much of each tile on
+// scalar address arithmetic. Here everything a tile reads (its partial
+// rows, the gate rows of its tokens and its LSEs) moves straight from memory
+// into LDS by buffer-to-LDS loads, which hold no registers while in flight,
+// two tiles ahead of the tile being merged; every load of a tile shares one
+// scalar base at its first token, with per-lane offsets fixed for the
+// launch. Workgroups keep one head and walk its tiles as the persistent
+// kernel's do, W_V[h] in registers; each tile's core rows are staged in LDS
+// and written at the next tile, 16 bytes a lane, so every token's 256 bytes
+// of the head go out as whole cache lines. NR = n partials per token (1:
+// copied, 2: merged); a tile has 16 / NR tokens, so a wave owns 2 / NR
+// tokens and 2 partial rows of every tile either way. Same arithmetic and
+// order of summation as the other kernels.
+constexpr int STREAM_NBUF = 3;  // tiles in LDS: the one merged and two in flight
+constexpr int LDS_WAVE_LSE = 256;  // one wave's LSE load: 64 lanes x 4 B
+
+template <int NR>
+struct StreamTile {
+  static constexpr int TT = TILE_T / NR;          // tokens per tile
+  static constexpr int TPW = TT / WAVES;          // tokens per wave
+  static constexpr int ROWS = 0;                  // rows: token slot tt, partial j at (tt NR + j) KiB
+  static constexpr int GATE = TILE_T * KVL * 2;   // gate rows: slot tt at GATE + 256 tt (head h's 128)
+  static constexpr int LSE = GATE + TT * VD * 2;  // LSEs: wave w's load at LSE + 256 w
+  static constexpr int BYTES = LSE + WAVES * LDS_WAVE_LSE;
+  static constexpr int LOADS = NR * TPW + TPW + 1;  // loads a wave issues per tile
+};
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8): at most n vector memory operations outstanding;
+// no LDS operation outstanding.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int WAIT_LGKM0 = 15 | (3 << 14) | (7 << 4);
+
+// A workgroup barrier that leaves vector memory loads in flight: the wave's
+// own LDS writes are complete, then s_barrier. (__syncthreads also waits
+// for every outstanding buffer-to-LDS load, which here are the next tiles'.)
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Where a workgroup's loads and stores go, fixed for the whole launch. The
+// streaming kernel takes only layouts where a (token, head) row, its gate
+// row and its LSEs move by a fixed stride per token (no request-major
+// offset), with strides that keep every offset within a tile below 2^31 (the
+// host checks): each tile's loads then use a scalar base at the tile's first
+// token and per-lane offsets computed here once.
+struct StreamAddr {
+  const uint8_t* o_h[2];  // partial j's row of token 0, head h
+  const uint8_t* g_h;     // gate row of token 0, head h
+  uint8_t* c_h;           // core row of token 0, head h
+  const uint8_t* l_h;     // LSE of partial 0, token 0, head h (the gate when there are none)
+  int o_stb, l_st4;       // bytes per token
+  int lse_tail;           // LSE bytes a token's loads span
+  uint32_t vrow[2];       // this lane's offset in the wave's k-th token's row
+  uint32_t vgate[2];      // .. in its gate row
+  uint32_t vlse;          // .. among the LSEs
+  uint32_t vout;          // this thread's piece of a staged output tile in core
+};
+
+template <int NR>
+__device__ __forceinline__ StreamAddr stream_addr(const KArgs& a, int h, int wave, int lane) {
+  using L = StreamTile<NR>;
+  StreamAddr s;
+  // the partials' strides are in bytes here, the LSEs' in elements
+  s.o_h[0] = a.o + (int64_t)h * a.o_sh;
+  s.o_h[1] = s.o_h[0] + (NR > 1 ? a.o_sj : 0);
+  s.g_h = a.gate + h * VD * 2;
+  s.c_h = a.core + h * VD * 2;
+  s.l_h = a.lse ? reinterpret_cast<const uint8_t*>(a.lse + (int64_t)h * a.l_sh) : a.gate;
+  s.o_stb = (int)a.o_st;
+  s.l_st4 = (int)(a.l_st * 4);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int tt = wave * L::TPW + (k < L::TPW ? k : 0);
+    s.vrow[k] = (uint32_t)(tt * s.o_stb + lane * 16);
+    s.vgate[k] = (uint32_t)(tt * GROWS * 2 + lane * 4);
+  }
+  // LSEs, 4 B a lane: with two partials lane j takes partial min(j, 1) of
+  // the wave's token; with one, lane 0 the LSE of the wave's first token and
+  // the other lanes that of its second
+  if constexpr (NR == 2) {
+    s.vlse = (uint32_t)(wave * s.l_st4 + min(lane, 1) * (int)(a.l_sj * 4));
+    s.lse_tail = (int)(a.l_sj * 4) + 4;
+  } else {
+    s.vlse = (uint32_t)((wave * 2 + min(lane, 1)) * s.l_st4);
+    s.lse_tail = 4;
+  }
+  s.vout = (uint32_t)((threadIdx.x >> 4) * GROWS * 2 + (threadIdx.x & 15) * 16);
+  return s;
+}
+
+// The loads of the tile [t0, tend) into its LDS buffer: every wave issues
+// exactly StreamTile<NR>::LOADS of them, for every tile index, also past its
+// last tile, so the number in flight is fixed. The rows and LSEs of tokens
+// past tend or the batch end, and the gate rows of tokens past tend, lie
+// beyond the end of their buffer resource (each token's bytes start past the
+// previous token's end): nothing is read, and what the LDS then holds is
+// never used. Without LSEs the LSE resource has zero bytes.
+template <int NR>
+__device__ __forceinline__ void stream_issue(const KArgs& a, const StreamAddr& s, int t0, int tend, int batch_end,
+                                             int wave, uint8_t* buf) {
+  using L = StreamTile<NR>;
+  const int live = max(0, tend - t0);                 // tokens of the tile
+  const int use = max(0, min(tend, batch_end) - t0);  // .. with partials to read
+  const uint64_t orow = (uint64_t)(uint32_t)t0 * (uint32_t)s.o_stb;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s.o_h[j] + orow), (short)0, use ? (use - 1) * s.o_stb + KVL * 2 : 0, BUF_WORD3);
+#pragma unroll
+    for (int k = 0; k < L::TPW; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + L::ROWS + ((wave * L::TPW + k) * NR + j) * KVL * 2),
+                                               16, s.vrow[k], 0, 0, NT_ROWS ? 2 : 0);  // 2: nt
+  }
+  {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s.g_h + (uint64_t)(uint32_t)t0 * (GROWS * 2)), (short)0,
+        live ? (live - 1) * (GROWS * 2) + VD * 2 : 0, BUF_WORD3);
+#pragma unroll
+    for (int k = 0; k < L::TPW; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + L::GATE + (wave * L::TPW + k) * VD * 2), 4,
+                                               s.vgate[k], 0, 0, 2);
+  }
+  {
+    const bool have = a.lse != nullptr && use > 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s.l_h + (a.lse ? (uint64_t)(uint32_t)t0 * (uint32_t)s.l_st4 : 0)), (short)0,
+        have ? (use - 1) * s.l_st4 + s.lse_tail : 0, BUF_WORD3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + L::LSE + wave * LDS_WAVE_LSE), 4, s.vlse, 0, 0, 0);
+  }
+}
+
+// The merge weights of two partials from their raw LSEs (wave-uniform), as
+// wave-uniform bits: the same values, bit for bit, as lse_to_weights over a
+// wave whose other lanes hold -inf (the maximum of two values is exact, each
+// exp is the same call on the same argument, and adding the zeros of the
+// other lanes to e0 + e1 leaves it unchanged), without its two 64-lane
+// reductions: lane 0 computes e0 and its weight, the other lanes e1 and its.
+__device__ __forceinline__ void two_weights(float l0, float l1, int& w0, int& w1) {
+  l0 = sane(l0);
+  l1 = sane(l1);
+  float m = fmaxf(l0, l1);
+  if (m == -INFINITY) m = 0.f;
+  const float e = expf(((threadIdx.x & 63) ? l1 : l0) - m);
+  const float tot = lane_f(e, 0) + lane_f(e, 1);
+  const float w = (tot == 0.f || e == 0.f) ? 0.f : e / tot;
+  w0 = __float_as_int(lane_f(w, 0));
+  w1 = __float_as_int(lane_f(w, 1));
+}
+
+// Write the staged output tile (final core values) of the tokens [t0, tend)
+// of head h: thread i writes piece i, 16 bytes of token i / 16, so each
+// token's 256 bytes of the head go out whole. Every thread stores, with no
+// branch: pieces of tokens past the tile (threads 16 TT and up included) lie
+// beyond the end of the buffer resource and are dropped. The stored value is
+// returned so that the caller keeps it live until the loop's next wait, when
+// the store has certainly read it: the compiler then never reuses its
+// registers early, which would make it wait for every load in flight.
+template <int TT>
+__device__ __forceinline__ uint4 stream_flush(const StreamAddr& s, int t0, int tend, const uint8_t* s_out) {
+  const int tok = min((int)(threadIdx.x >> 4), TILE_T - 1);
+  const uint4 v = *reinterpret_cast<const uint4*>(s_out + tok * OUT_ROW + (threadIdx.x & 15) * 16);
+  const int live = max(0, tend - t0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      s.c_h + (uint64_t)(uint32_t)min(t0, tend) * (GROWS * 2), (short)0, live ? (live - 1) * (GROWS * 2) + VD * 2 : 0,
+      BUF_WORD3);
+  __builtin_amdgcn_raw_buffer_store_b128((v4u){v.x, v.y, v.z, v.w}, r, s.vout, 0, 2);  // 2: nt
+  return v;
+}
+
+// One tile of the streaming kernel: tile `it` is in LDS buffer `cur`; the
+// loads of tile it + 2 go to buffer `ahead` (the one tile it - 1 used); the
+// output staged for tile it - 1 (tokens p0 .. pend) is written first, and
+// this tile's goes to s_out. The three buffers are distinct LDS variables,
+// named at compile time in each step: the compiler then knows that reading
+// `cur` does not touch what the loads in flight write (`ahead` and the third
+// buffer), and leaves them in flight instead of waiting for all of them
+// before the first read.
+template <bool COPY, int NR>
+__device__ __forceinline__ void stream_step(const KArgs& a, const TileSched& ts, int it, int h, int wave, int lane,
+                                            int batch_end, const StreamAddr& sad, const uint4 wv[4], int sa,
+                                            const uint8_t* cur, uint8_t* ahead, uint8_t* s_codes, uint8_t* s_scales,
+                                            uint8_t* s_out, int& p0, int& pend) {
+  using L = StreamTile<NR>;
+  constexpr int TT = L::TT;
+  const int tl = lane & 15;
+  const int kb = lane >> 4;
+  // Tile it has landed when at most tile it + 1's loads are outstanding
+  // (loads complete in order, and a step's core stores come before the loads
+  // it issues); after the barrier every wave's share of it has, and every
+  // wave is done with tile it - 1: the codes and the staged output.
+  __builtin_amdgcn_s_waitcnt(wait_vm(L::LOADS));
+  lds_barrier();
+  const uint4 flushed = stream_flush<TT>(sad, p0, pend, s_out);
+  int t0, tend;
+  tile_span<TT>(ts, it, t0, tend);
+  // ---- merge (or copy) + quantise this wave's tokens
+#pragma unroll
+  for (int k = 0; k < L::TPW; ++k) {
+    const int tt = wave * L::TPW + k;
+    const int t = t0 + tt;
+    const bool live = t < tend, empty = t >= batch_end;
+    const uint4 v0 = *reinterpret_cast<const uint4*>(cur + L::ROWS + tt * NR * KVL * 2 + lane * 16);
+    // lanes 0 and 1 of the wave's LSE load: the LSEs of its tokens (one
+    // partial) or of its token's two partials
+    const float2 l2 = *reinterpret_cast<const float2*>(cur + L::LSE + wave * LDS_WAVE_LSE);
+    if constexpr (COPY) {
+      copy_stage(a, t, tt, h, lane, live, empty, v0, k ? l2.y : l2.x, s_codes, s_scales);
+    } else {
+      const uint4 v1 = *reinterpret_cast<const uint4*>(cur + L::ROWS + (tt * NR + 1) * KVL * 2 + lane * 16);
+      uint32_t lat[4] = {0u, 0u, 0u, 0u};
+      if (live && !empty) {
+        int w0, w1;
+        two_weights(l2.x, l2.y, w0, w1);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (w0 & 0x7FFFFFFF) fma_row(__int_as_float(w0), v0, acc);
+        if (w1 & 0x7FFFFFFF) fma_row(__int_as_float(w1), v1, acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lat[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
+      }
+      quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
+    }
+  }
+  lds_barrier();  // the codes are complete; every wave is done with s_out and tile it - 1's buffer
+  // Tile it + 2's loads go out now, after the merge: the scalar work of
+  // forming them overlaps the MFMAs below instead of delaying the merge.
+  {
+    int n0, nend;
+    tile_span<TT>(ts, it + STREAM_NBUF - 1, n0, nend);
+    stream_issue<NR>(a, sad, n0, nend, batch_end, wave, ahead);
+  }
+
+  // ---- W_UV, gate, stage: the lane holds rows v0..v0+3 (v0 = 16 wave +
+  // 4 kb) of token slot tl; its gate values come from the tile's LDS buffer
+  // (slots past an 8-token tile read bytes that are never stored)
+  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const uint8_t* brow = s_codes + tl * 16;
+    acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
+    acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
+  }
+  // stored unconditionally before any lane-dependent branch: the MFMAs run
+  // with the whole wave active
+  const uint2 g4 = *reinterpret_cast<const uint2*>(cur + L::GATE + tl * VD * 2 + (wave * 16 + kb * 4) * 2);
+  const uint2 ab = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+  *reinterpret_cast<uint2*>(s_out + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
+      make_uint2(pack_bf16(bf_lo(ab.x) * bf_lo(g4.x), bf_hi(ab.x) * bf_hi(g4.x)),
+                 pack_bf16(bf_lo(ab.y) * bf_lo(g4.y), bf_hi(ab.y) * bf_hi(g4.y)));
+  p0 = t0;
+  pend = tend;
+  asm volatile("" ::"v"(flushed.x), "v"(flushed.y), "v"(flushed.z), "v"(flushed.w));
+}
+
+template <bool COPY, int NR>
+__global__ __launch_bounds__(THREADS) void mla_post_stream_kernel(const KArgs a, int wg_per_head) {
+  static_assert(COPY == (NR == 1), "one partial is copied, two are merged");
+  static_assert(STREAM_NBUF == 3, "the tile loop names three buffers");
+  using L = StreamTile<NR>;
+  constexpr int TT = L::TT;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf0[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf1[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf2[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[LDS_OUT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int h, slot;
+  head_and_slot(h, slot);
+  const TileSched ts = tile_sched<TT>(a.S, wg_per_head, slot, true);
+  const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
+
+  // W_V[h] first (the first MFMAs wait for it anyway), then the first tiles
+  uint4 wv[4];
+  int sa = 0;
+  load_wv(a, h, wave, lane & 15, lane >> 4, wv, sa);
+  const StreamAddr sad = stream_addr<NR>(a, h, wave, lane);
+  {
+    int t0, tend;
+    tile_span<TT>(ts, 0, t0, tend);
+    stream_issue<NR>(a, sad, t0, tend, batch_end, wave, s_buf0);
+    tile_span<TT>(ts, 1, t0, tend);
+    stream_issue<NR>(a, sad, t0, tend, batch_end, wave, s_buf1);
+  }
+  // 8-token tiles: MFMA columns 8..15 never hold a token, zero codes once
+  if constexpr (TT < TILE_T) empty_slot(a, TT + wave, h, lane, s_codes, s_scales);
+
+  int p0 = a.S, pend = a.S;  // tokens of the tile whose output is staged
+#pragma unroll 1
+  for (int it = 0; it < ts.count; it += STREAM_NBUF) {
+    stream_step<COPY, NR>(a, ts, it, h, wave, lane, batch_end, sad, wv, sa, s_buf0, s_buf2, s_codes, s_scales, s_out,
+                          p0, pend);
+    if (it + 1 >= ts.count) break;
+    stream_step<COPY, NR>(a, ts, it + 1, h, wave, lane, batch_end, sad, wv, sa, s_buf1, s_buf0, s_codes, s_scales,
+                          s_out, p0, pend);
+    if (it + 2 >= ts.count) break;
+    stream_step<COPY, NR>(a, ts, it + 2, h, wave, lane, batch_end, sad, wv, sa, s_buf2, s_buf1, s_codes, s_scales,
+                          s_out, p0, pend);
+  }
+  lds_barrier();
+  stream_flush<TT>(sad, p0, pend, s_out);
+  // the loads issued for tile indices past the last are still in flight:
+  // they read nothing, but the wave waits for them (and its stores) before
+  // it ends
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+}
+
 // ---------------------------------------------------------------- stand-alone quantiser
 
 constexpr int QWAVES = 4;
@@ -1165,10 +1497,51 @@ int split_tile(int n, int S, int cus) {
 // with LSEs; the split-rows kernel for many partials and few tokens; else
 // the persistent kernel. One partial is copied. mla_post launches exactly
 // this.
+// Workgroups per head of the streaming kernel: as many as are resident at
+// once (its LDS ring and buffers: 2 per CU with three tile buffers, 3 with
+// two), rounded down to a multiple of 8 so that the 12 heads of a slot share
+// an XCD (40 or 64 at 256 CUs).
+constexpr int STREAM_WG_PER_CU = 2;
+int stream_workgroups_per_head(int cus) { return max(XCDS, (STREAM_WG_PER_CU * cus / NH) / XCDS * XCDS); }
+
+// Whether the streaming kernel takes the call: one or two partials, no KV
+// length masks, a layout where rows and LSEs move by a fixed stride per token
+// (no request-major offset), each token's row past the previous one's end
+// (o_st >= 512) and its LSEs past the previous ones (l_st >= 1), offsets
+// within a tile below 2^31, and at least STREAM_MIN_TOKENS_PER_CU tokens per
+// CU. Measured at 256 CUs against the one-tile and persistent kernels, with
+// the large decode batch's distributions: ahead from S = 1536 with one
+// partial (with an LSE: S = 1536 12.7 -> 10.6 us, 4096 20.2 -> 17.7, 8192
+// 35.6 -> 29.9, 16384 66.1 -> 56.7; without: 8192 31.7 -> 29.6) and with two
+// (S = 1536 14.8 -> 14.5, 4096 30.5 -> 28.1, 8192 56.4 -> 50.3, 16384 107.3
+// -> 96.7), behind at S = 1024 (one partial 8.5 -> 9.0 us, two 10.6 -> 12.2).
+constexpr int STREAM_MIN_TOKENS_PER_CU = 6;
+bool stream_takes(const mla_post_args* a, int cus) {
+  if (a->n > 2 || a->kv_lens || a->o_sr) return false;
+  const int64_t lim = (int64_t(1) << 31) - 4096;
+  if (a->o_st < KVL || a->o_st > lim / (2 * TILE_T)) return false;
+  if (a->lse && (a->l_sr || a->l_st < 1 || a->l_st > lim / (8 * TILE_T) || a->l_sj > lim / 8)) return false;
+  return (int64_t)a->S >= (int64_t)STREAM_MIN_TOKENS_PER_CU * cus;
+}
+
 mla_post_plan make_plan(const mla_post_args* a, int cus) {
   mla_post_plan p;
   memset(&p, 0, sizeof(p));
   p.cus = cus;
+  if (stream_takes(a, cus)) {
+    const int tt = TILE_T / a->n;
+    p.kernel = MLA_POST_KERNEL_STREAM;
+    p.tile_tokens = tt;
+    p.rows_held = a->n;
+    p.lse_chunks = 1;
+    p.workgroups_per_head = stream_workgroups_per_head(cus);
+    p.workgroups = NH * p.workgroups_per_head;
+    if (tt == TILE_T)
+      tile_counts<TILE_T>(a->S, p.workgroups_per_head, true, p.full_tiles, p.short_tokens);
+    else
+      tile_counts<TILE_T / 2>(a->S, p.workgroups_per_head, true, p.full_tiles, p.short_tokens);
+    return p;
+  }
   // one partial (with or without an LSE) is copied rather than merged
   const bool copy = a->n == 1;
   const int S = a->S, n = a->n;
@@ -1278,6 +1651,9 @@ int launch_plan(const KArgs& k, const mla_post_plan& p, bool copy, hipStream_t s
   }
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
   const int wph = p.workgroups_per_head;
+  if (p.kernel == MLA_POST_KERNEL_STREAM)
+    return copy ? launch(mla_post_stream_kernel<true, 1>, grid, block, stream, k, wph)
+                : launch(mla_post_stream_kernel<false, 2>, grid, block, stream, k, wph);
   if (copy) return launch(mla_post_kernel<true, 1, 0>, grid, block, stream, k, wph);
   if (p.pair_rows == PF_ROWS / 2) return launch(mla_post_kernel<false, 1, PF_ROWS / 2>, grid, block, stream, k, wph);
   if (p.lse_chunks == 1) return launch(mla_post_kernel<false, 1, 0>, grid, block, stream, k, wph);

@@ -70,14 +70,25 @@ TABLE = [
     # both tokens' rows a tile ahead for n <= 4 with LSEs
     ((3, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
     ((4, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
-    # two partials with LSEs: the one-tile instance at every size up to 2^20
-    ((2, 8200, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=513)),
-    ((2, 1 << 20, True), dict(kernel="one_tile", tile_tokens=16, workgroups_per_head=65536)),
-    ((2, (1 << 20) + 16, True), dict(kernel="persistent", workgroups_per_head=64)),
-    # one partial, with an LSE or not, is copied: as without LSEs, the
-    # one-tile instance while it fits, else the persistent kernel
-    ((1, 4096, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
-    ((1, 1 << 20, True), dict(kernel="persistent", workgroups_per_head=64)),
+    # two partials with LSEs: the one-tile instance below 6 tokens per CU
+    # (S = 1536 at 256 CUs), the streaming kernel from there (8-token tiles,
+    # 40 workgroups per head, leftover tokens dealt out evenly)
+    ((2, 1535, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=96)),
+    ((2, 1536, True), dict(kernel="stream", tile_tokens=8, rows_held=2, workgroups_per_head=40, workgroups=480,
+                           full_tiles=4, short_tokens=7)),
+    ((2, 8200, True), dict(kernel="stream", tile_tokens=8, rows_held=2, workgroups_per_head=40, full_tiles=25,
+                           short_tokens=5)),
+    ((2, 1 << 20, True), dict(kernel="stream", tile_tokens=8, workgroups_per_head=40)),
+    # one partial, with an LSE or not, is copied: the one-tile instance while
+    # it fits, the persistent kernel up to 6 tokens per CU, then the
+    # streaming kernel (16-token tiles)
+    ((1, 1535, True), dict(kernel="persistent", workgroups_per_head=40, pair_rows=0)),
+    ((1, 1536, True), dict(kernel="stream", tile_tokens=16, rows_held=1, workgroups_per_head=40, full_tiles=2,
+                           short_tokens=7)),
+    ((1, 4096, True), dict(kernel="stream", tile_tokens=16, rows_held=1, workgroups_per_head=40, full_tiles=6,
+                           short_tokens=7)),
+    ((1, 4096, False), dict(kernel="stream", tile_tokens=16, rows_held=1)),
+    ((1, 1 << 20, True), dict(kernel="stream", workgroups_per_head=40)),
     ((5, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
     # the one-round rule (65 to 96 tiles) and the leftover deal
     ((16, 1100, True), dict(kernel="persistent", workgroups_per_head=40, workgroups=480, full_tiles=1, short_tokens=12)),
@@ -140,6 +151,9 @@ def test_routing_table_at_256_cus(key, expect):
     elif p["kernel"] == "split_rows":
         assert p["full_tiles"] == 0 and p["short_tokens"] == 0 and p["pair_rows"] == 0
         assert p["workgroups"] == 12 * p["workgroups_per_head"]
+    elif p["kernel"] == "stream":
+        assert p["tile_tokens"] == 16 // key[0] and p["rows_held"] == key[0] and p["pair_rows"] == 0
+        assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["workgroups_per_head"] % 8 == 0
     else:
         assert p["tile_tokens"] == 16 and p["rows_held"] == 0
         assert p["pair_rows"] == (4 if key[2] and 2 <= key[0] <= 4 else 0)
@@ -160,16 +174,17 @@ def test_invalid_arguments_give_the_check_status():
 
 
 def covered(p, S):
-    """Token -> number of persistent workgroups of one head that own it, from
-    the plan's fields and the schedule rule (full tiles at stride k, then the
-    leftover tokens in consecutive runs of short_tokens, slot by slot)."""
-    k, main, chunk = p["workgroups_per_head"], p["full_tiles"], p["short_tokens"]
+    """Token -> number of persistent or streaming workgroups of one head that
+    own it, from the plan's fields and the schedule rule (full tiles at
+    stride k, then the leftover tokens in consecutive runs of short_tokens,
+    slot by slot)."""
+    k, main, chunk, tt = p["workgroups_per_head"], p["full_tiles"], p["short_tokens"], p["tile_tokens"]
     count = np.zeros(S, dtype=np.int64)
     for slot in range(k):
         for i in range(main):
-            t0 = (slot + i * k) * 16
-            count[t0 : t0 + 16] += 1
-        base = main * 16 * k
+            t0 = (slot + i * k) * tt
+            count[t0 : t0 + tt] += 1
+        base = main * tt * k
         t0 = base + slot * chunk
         if chunk and t0 < S:
             count[t0 : min(t0 + chunk, S)] += 1
@@ -186,13 +201,14 @@ def test_schedule_covers_every_token_once(cus):
                         1537, 2064, 4096, 4112, 9000]
                        + list(rng.integers(1, 20000, size=60))))
     for S in sizes:
-        for n, lse in ((1, False), (1, True), (4, True), (6, True), (16, True), (20, True), (100, True), (256, True)):
+        for n, lse in ((1, False), (1, True), (2, True), (4, True), (6, True), (16, True), (20, True), (100, True),
+                       (256, True)):
             p = plan(n, int(S), lse, cus)
             assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["cus"] == cus
             if p["kernel"] in ("one_tile", "split_rows"):
                 assert p["workgroups_per_head"] * p["tile_tokens"] >= S > (p["workgroups_per_head"] - 1) * p["tile_tokens"]
                 continue
-            assert 0 <= p["short_tokens"] <= 16
+            assert 0 <= p["short_tokens"] <= p["tile_tokens"]
             c = covered(p, int(S))
             assert np.all(c == 1), (n, S, cus, p)
 
