@@ -324,34 +324,43 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
     return out
 
 
-def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16) -> dict:
+def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16, no_lse: bool = False) -> dict:
     """Microseconds per call and the roofline fraction at several batch sizes
     S, with the large decode batch's distributions (16 splits unless given,
     o ~ N(0, 2), lse ~ N(8, 6) with 5% -inf, seed 4), generated once at the
     largest size; each size takes the first S tokens of it (strided views, as
-    a caller would pass them)."""
+    a caller would pass them). no_lse: one partial without LSEs instead (o ~
+    N(0, 1), seed 3)."""
     import numpy as np
 
     import synth
 
     smax = max(sizes)
-    log(f"generating {splits} splits x {smax} tokens ({splits * smax * 12 * 1024 / 1e6:.0f} MB of partials)")
-    w = synth.dense_splits(f"sweep_n{splits}_S{smax}", splits, smax, seed=4, o_sigma=2.0, lse_normal=(8.0, 6.0),
-                           p_neg_inf=0.05)
+    if no_lse:
+        splits = 1
+        log(f"generating one partial without LSEs x {smax} tokens")
+        w = synth.single_partial(f"sweep_nolse_S{smax}", smax, seed=3)
+    else:
+        log(f"generating {splits} splits x {smax} tokens ({splits * smax * 12 * 1024 / 1e6:.0f} MB of partials)")
+        w = synth.dense_splits(f"sweep_n{splits}_S{smax}", splits, smax, seed=4, o_sigma=2.0, lse_normal=(8.0, 6.0),
+                               p_neg_inf=0.05)
     d = device_setup(w, m, torch)
-    live_by_token = np.isfinite(w.lse_view()).sum(axis=(0, 2))
+    lse_bytes = 0 if no_lse else splits * 12 * 4
+    live_by_token = (np.full(smax, 12) if no_lse else np.isfinite(w.lse_view()).sum(axis=(0, 2)))
     rows = []
     for S in sizes:
-        call = m.prepare(d["o"][:, :S], d["lse"][:, :S], d["w_v"], d["w_s"], d["gate"][:S], d["core"][:S])
+        lse = None if no_lse else d["lse"][:, :S]
+        call = m.prepare(d["o"][:, :S], lse, d["w_v"], d["w_s"], d["gate"][:S], d["core"][:S])
         t = time_gpu(call, steps, warmup, torch)
         us = 1e3 * t["event_ms"] / steps
-        alg = int(live_by_token[:S].sum()) * 1024 + splits * S * 12 * 4 + W_V_BYTES + 2 * S * 1536 * 2
+        alg = int(live_by_token[:S].sum()) * 1024 + S * lse_bytes + W_V_BYTES + 2 * S * 1536 * 2
         gbps = alg / (us * 1e-6) / 1e9
         rows.append({"S": S, "us_per_call": round(us, 3), "GBps": round(gbps, 1),
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "tokens_per_s": round(S / (us * 1e-6), 1),
-                     "alg_bytes": alg, "plan": m.plan(d["o"][:, :S], d["lse"][:, :S], d["w_v"], d["w_s"], d["gate"][:S])})
+                     "alg_bytes": alg, "plan": m.plan(d["o"][:, :S], lse, d["w_v"], d["w_s"], d["gate"][:S])})
         log(f"S={S}: {rows[-1]}")
-    return {"size_sweep": rows, "workload": f"{splits} splits, large decode distributions, first S tokens", "steps": steps}
+    what = "one partial without LSEs" if no_lse else f"{splits} splits, large decode distributions"
+    return {"size_sweep": rows, "workload": f"{what}, first S tokens", "steps": steps}
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD's published figure
@@ -498,6 +507,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--sizes", help="comma-separated batch sizes S: print a size sweep (one JSON object) instead")
     ap.add_argument("--splits", type=int, default=16, help="partials per (token, head) of the size sweep")
+    ap.add_argument("--no-lse", action="store_true", help="size sweep of one partial without LSEs")
     ap.add_argument(
         "--traffic-from",
         nargs=4,
@@ -536,7 +546,7 @@ def main() -> int:
         torch.cuda.set_device(0)
         m.load()
         sizes = [int(x) for x in args.sizes.split(",")]
-        print(json.dumps(size_sweep(sizes, args.steps, args.warmup, m, torch, args.splits)))
+        print(json.dumps(size_sweep(sizes, args.steps, args.warmup, m, torch, args.splits, args.no_lse)))
         return 0
 
     log(f"generating the {args.workload} workload (seeded, 805 MB of partials)")
