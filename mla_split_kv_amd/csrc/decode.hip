@@ -295,8 +295,13 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
 
 template <bool FUSED>
 __global__ __launch_bounds__(DTHREADS) void mla_decode_kernel(const DArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  __shared__ int s_last;
+  // One LDS variable (the flag below lives past the KV blocks): with a single
+  // one the compiler does not order this wave's LDS reads behind the
+  // buffer-to-LDS loads in flight, whose completion the block loop waits for
+  // itself; with several it treats every access to the KV array as touching
+  // the block being loaded.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES + 16];
+  int* const s_last = reinterpret_cast<int*>(lds + LDS_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -336,25 +341,29 @@ __global__ __launch_bounds__(DTHREADS) void mla_decode_kernel(const DArgs a) {
   // rows 8 w .. 8 w + 7 (one instruction: 8 lanes per row). Rows past the
   // split's end load the split's last row instead (their scores are masked
   // to -inf, so their probabilities are 0 and their finite values add 0).
+  const int vlane16 = lane * 16;
+  int tail_off = 0;  // the rotary loads' per-lane offset, kept live until the block's reads are done
   auto load_block = [&](int b) {
-    const int rows = min(nrows - b * BC, BC);
+    const int rows = min(nrows - b * BC, BC);  // 0 for block 0 of an empty split: nothing is read
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.kv + (int64_t)(k0 + b * BC) * a.kv_st), (short)0,
-        (rows - 1) * (int)a.kv_st + DQK * 2, BUF_WORD3);
+        rows > 0 ? (rows - 1) * (int)a.kv_st + DQK * 2 : 0, BUF_WORD3);
     uint8_t* dst = lds + (b % NBUF) * BLOCK_BYTES;
+    // the row's offset is the same for the whole wave: the scalar offset;
+    // the lane's, fixed for the launch, the vector one (so no vector
+    // register is written per block for them, which the compiler would then
+    // have to keep from reuse until the loads had read it)
 #pragma unroll
     for (int i = 0; i < BC / DW; ++i) {
       const int row = wave + DW * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + row * MROW), 16,
-                                               min(row, rows - 1) * (int)a.kv_st + lane * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + row * MROW), 16, vlane16,
+                                               max(min(row, rows - 1), 0) * (int)a.kv_st, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < BC / 8 / DW; ++i) {
       const int grp = wave + DW * i;  // rows 8 grp .. 8 grp + 7
-      const int row = 8 * grp + (lane >> 3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + TAIL + 8 * grp * TROW), 16,
-                                               min(row, rows - 1) * (int)a.kv_st + KVL * 2 + (lane & 7) * 16, 0, 0,
-                                               0);
+      tail_off = max(min(8 * grp + (lane >> 3), rows - 1), 0) * (int)a.kv_st + KVL * 2 + (lane & 7) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + TAIL + 8 * grp * TROW), 16, tail_off, 0, 0, 0);
     }
   };
 
@@ -367,9 +376,21 @@ __global__ __launch_bounds__(DTHREADS) void mla_decode_kernel(const DArgs a) {
   v4f acc[NCOLT];                    // O^T: value columns 16 c + 4 g + i, query c16
 #pragma unroll
   for (int c = 0; c < NCOLT; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < min(nblk, NBUF - 1); ++b) load_block(b);
-#pragma unroll 1
-  for (int b = 0; b < nblk; ++b) {
+  // Block 0's loads (issued even for an empty split, reading nothing, so
+  // that the count of loads in flight is known here), then the queries are
+  // waited for (block 0 stays in flight; the compiler then knows the queries
+  // are in registers and does not wait again inside the loop), then blocks 1
+  // and 2.
+  load_block(0);
+#pragma unroll
+  for (int k = 0; k < KSTEPS; k += 6) {
+    const uint4 q0 = __builtin_bit_cast(uint4, qreg[k]), q1 = __builtin_bit_cast(uint4, qreg[k + 1]),
+                q2 = __builtin_bit_cast(uint4, qreg[k + 2]), q3 = __builtin_bit_cast(uint4, qreg[k + 3]),
+                q4 = __builtin_bit_cast(uint4, qreg[k + 4]), q5 = __builtin_bit_cast(uint4, qreg[k + 5]);
+    asm volatile("" ::"v"(q0.x), "v"(q1.x), "v"(q2.x), "v"(q3.x), "v"(q4.x), "v"(q5.x));
+  }
+  for (int b = 1; b < min(nblk, NBUF - 1); ++b) load_block(b);
+  auto block = [&](int b) {
     // Block b is complete when at most the loads of the blocks issued after
     // it are outstanding (vector memory operations complete in order); then
     // every wave's share of it is, after the barrier. The barrier also tells
@@ -436,19 +457,51 @@ __global__ __launch_bounds__(DTHREADS) void mla_decode_kernel(const DArgs a) {
                                (__bf16)s[1][0], (__bf16)s[1][1], (__bf16)s[1][2], (__bf16)s[1][3]};
       // V^T operands by transposed LDS reads: in each 16-lane group, lane i
       // points at row base + i / 4, columns 16 c + 4 (i mod 4) .. + 3, and
-      // lane j receives rows base .. base + 3 of column 16 c + j
-      const int o0 = (b % NBUF) * BLOCK_BYTES + (4 * g + (c16 >> 2)) * MROW + (c16 & 3) * 8;
+      // lane j receives rows base .. base + 3 of column 16 c + j. The reads
+      // are issued by hand, four column tiles at a time, each batch ending in
+      // its own wait for them: the compiler cannot tell which LDS block the
+      // builtin's reads touch, so for it it waits for every load in flight
+      // (the next blocks' too) first. Block b is complete and visible here
+      // (the wait and barrier above), and the next barrier comes after this
+      // wave's reads have returned.
+      const uint32_t vaddr = (uint32_t)(uintptr_t)(lds + (b % NBUF) * BLOCK_BYTES + (4 * g + (c16 >> 2)) * MROW +
+                                                   (c16 & 3) * 8);
 #pragma unroll
-      for (int c = 0; c < NCOLT; ++c) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + o0 + 32 * c));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + o0 + 16 * MROW + 32 * c));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[c], 0, 0, 0);
+      for (int c0 = 0; c0 < NCOLT; c0 += 4) {
+        v2u lo0, lo1, lo2, lo3, hi0, hi1, hi2, hi3;
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8 offset:%9\n"
+            "ds_read_b64_tr_b16 %1, %8 offset:%10\n"
+            "ds_read_b64_tr_b16 %2, %8 offset:%11\n"
+            "ds_read_b64_tr_b16 %3, %8 offset:%12\n"
+            "ds_read_b64_tr_b16 %4, %8 offset:%13\n"
+            "ds_read_b64_tr_b16 %5, %8 offset:%14\n"
+            "ds_read_b64_tr_b16 %6, %8 offset:%15\n"
+            "ds_read_b64_tr_b16 %7, %8 offset:%16\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(lo0), "=v"(lo1), "=v"(lo2), "=v"(lo3), "=v"(hi0), "=v"(hi1), "=v"(hi2), "=v"(hi3)
+            : "v"(vaddr), "i"(32 * c0), "i"(32 * c0 + 32), "i"(32 * c0 + 64), "i"(32 * c0 + 96),
+              "i"(16 * MROW + 32 * c0), "i"(16 * MROW + 32 * c0 + 32), "i"(16 * MROW + 32 * c0 + 64),
+              "i"(16 * MROW + 32 * c0 + 96));
+        const v2u lo[4] = {lo0, lo1, lo2, lo3}, hi[4] = {hi0, hi1, hi2, hi3};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const v4u w = {lo[c].x, lo[c].y, hi[c].x, hi[c].y};
+          acc[c0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb, acc[c0 + c], 0, 0, 0);
+        }
       }
     }
     // this wave's LDS reads of block b have returned before the next barrier
     __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
-  }
+    asm volatile("" ::"v"(tail_off), "v"(vlane16));
+  };
+  // The first block outside the loop: there the compiler sees that the
+  // query loads precede the KV loads and waits only for them, where at the
+  // top of a loop it cannot tell the first pass from later ones and would
+  // wait for every KV block in flight.
+  if (nblk > 0) block(0);
+#pragma unroll 1
+  for (int b = 1; b < nblk; ++b) block(b);
   __syncthreads();
 
   // partials: bf16(O / sum) and ln(sum exp) of each query row (an empty split:
@@ -490,11 +543,11 @@ __global__ __launch_bounds__(DTHREADS) void mla_decode_kernel(const DArgs a) {
     // (an invalidation of the whole L2).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) s_last = __hip_atomic_fetch_add(a.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n - 1;
+    if (tid == 0) *s_last = __hip_atomic_fetch_add(a.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n - 1;
     __syncthreads();
     // the same value on every lane: read as a scalar, so the branch is uniform
     // and the consumer's MFMAs run with the whole wave active
-    if (!__builtin_amdgcn_readfirstlane(s_last)) return;
+    if (!__builtin_amdgcn_readfirstlane(*s_last)) return;
     consume(a, r, lds);
     if (tid == 0) __hip_atomic_store(a.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
