@@ -26,12 +26,14 @@
  *
  * The handoff is this library's own, not the page's: no workgroup ever
  * waits for another. Each (request, split) workgroup writes its partials to
- * the workspace and fences them at device scope, then adds 1 to its
- * request's counter (a vector atomic); the workgroup that brings the counter
- * to n merges that request's partials and runs W_UV for its tokens, then
- * sets the counter back to 0. So the launch cannot deadlock whatever order
- * or placement its workgroups get, and a call leaves the counters as it
- * found them.
+ * the workspace with stores that go through to the device's coherence point
+ * (device-scope cache policy), waits for them to complete, then adds 1 to
+ * its request's counter (a vector atomic at device scope); the workgroup
+ * that brings the counter to n reads that request's partials with loads of
+ * the same policy, merges them and runs W_UV for its tokens, then sets the
+ * counter back to 0. So the launch cannot deadlock whatever order or
+ * placement its workgroups get, and a call leaves the counters as it found
+ * them.
  *
  * Conventions as in mla_post.h (C linkage, caller-owned device memory,
  * asynchronous on the caller's stream, MLA_POST_* status codes, validation
