@@ -63,7 +63,7 @@ constexpr int DW = 4;                        // waves per workgroup
 constexpr int DTHREADS = DW * 64;
 constexpr int BC = 32;                       // KV rows per block (one MFMA K step of the value product)
 constexpr float RESCALE_AT = 8.f;            // base-2 headroom of the softmax reference
-constexpr int NBUF = 4;                      // LDS blocks: the one computed on and 3 in flight
+constexpr int NBUF = 2;                      // LDS blocks: the one computed on and the next in flight
 constexpr int MROW = KVL * 2 + 16;           // LDS bytes per block row of the 512 latent dims (+16 B skew)
 constexpr int TROW = (DQK - KVL) * 2;        // LDS bytes per block row of the 64 rotary dims
 constexpr int TAIL = BC * MROW;              // offset of a block's rotary part
@@ -81,8 +81,10 @@ constexpr int LDS_SCALES = 16 * NBLK;
 constexpr int CORE_ROW = GROWS * 2 + 16;
 constexpr int LDS_BYTES = NBUF * BLOCK_BYTES;
 static_assert(BC % (8 * DW) == 0 && LOADS_PER_WAVE <= 15, "whole loads per wave; the waits count them");
-static_assert(NH * (LDS_CODES + LDS_SCALES) + (MLA_DECODE_QMAX + 1) * CORE_ROW + MLA_DECODE_QMAX * NH * 64 * 4 <= LDS_BYTES,
-              "consumer fits the KV buffers");
+static_assert(NH * (LDS_CODES + LDS_SCALES) + ((MLA_DECODE_QMAX + 1) * CORE_ROW > MLA_DECODE_QMAX * NH * 64 * 4
+                                                    ? (MLA_DECODE_QMAX + 1) * CORE_ROW
+                                                    : MLA_DECODE_QMAX * NH * 64 * 4) <= LDS_BYTES,
+              "consumer fits the KV buffers (merge weights and staged core rows share bytes)");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -153,7 +155,9 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
   uint8_t* s_codes = lds;                        // [12][LDS_CODES]
   uint8_t* s_scales = lds + NH * LDS_CODES;      // [12][16 slots][16 blocks]
   uint8_t* s_core = s_scales + NH * LDS_SCALES;  // [q + 1 spare][CORE_ROW]
-  float* s_w = reinterpret_cast<float*>(s_core + (MLA_DECODE_QMAX + 1) * CORE_ROW);  // [4 waves][12][64] weights
+  // [4 waves][12][64] weights, in the same bytes as s_core: read only by the
+  // merge, s_core written only after the barrier that ends it
+  float* s_w = reinterpret_cast<float*>(s_core);
   const int qrows = NH * a.q;
   // token slots past q: zero codes, scale code 1 (MFMA columns of zeros)
   for (int i = tid; i < NH * NBLK * (16 - a.q); i += DTHREADS) {
@@ -294,7 +298,7 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
 // ---------------------------------------------------------------- the attention (and the fused launch)
 
 template <bool FUSED>
-__global__ __launch_bounds__(DTHREADS) void mla_decode_kernel(const DArgs a) {
+__global__ __launch_bounds__(DTHREADS, 2) void mla_decode_kernel(const DArgs a) {
   // One LDS variable (the flag below lives past the KV blocks): with a single
   // one the compiler does not order this wave's LDS reads behind the
   // buffer-to-LDS loads in flight, whose completion the block loop waits for
