@@ -963,30 +963,37 @@ __global__ __launch_bounds__(THREADS) void mla_post_split_kernel(const KArgs a) 
 // then reads only 16 KiB of rows; the persistent kernel keeps one tile's rows
 // in flight in registers and loads each tile's gate as it goes, so it waits
 // about one memory round trip per tile and spends much of each tile on
-// scalar address arithmetic. Here everything a tile reads (its partial
-// rows, the gate rows of its tokens and its LSEs) moves straight from memory
-// into LDS by buffer-to-LDS loads, which hold no registers while in flight,
-// two tiles ahead of the tile being merged; every load of a tile shares one
-// scalar base at its first token, with per-lane offsets fixed for the
-// launch. Workgroups keep one head and walk its tiles as the persistent
-// kernel's do, W_V[h] in registers; each tile's core rows are staged in LDS
-// and written at the next tile, 16 bytes a lane, so every token's 256 bytes
-// of the head go out as whole cache lines. NR = n partials per token (1:
-// copied, 2: merged); a tile has 16 / NR tokens, so a wave owns 2 / NR
-// tokens and 2 partial rows of every tile either way. Same arithmetic and
-// order of summation as the other kernels.
-constexpr int STREAM_NBUF = 3;  // tiles in LDS: the one merged and two in flight
-constexpr int LDS_WAVE_LSE = 256;  // one wave's LSE load: 64 lanes x 4 B
+// scalar address arithmetic. Here a tile's partial rows move straight from
+// memory into LDS by buffer-to-LDS loads, which hold no registers while in
+// flight, and its gate values and LSEs (a few bytes a lane) into registers,
+// issued together three tiles ahead of the tile being merged. Each wave
+// loads and merges only its own tokens' rows, so a tile needs one barrier,
+// between the merge and the MFMAs; the row buffer is refilled as soon as
+// the wave has merged it, and the codes and the staged output have a buffer
+// per tile in flight. Every load of a tile shares one scalar base at its
+// first token, with per-lane offsets fixed for the launch. Workgroups keep
+// one head and walk its tiles as the persistent kernel's do, W_V[h] in
+// registers; each tile's core rows are staged in LDS and written at the next
+// tile, 16 bytes a lane, so every token's 256 bytes of the head go out as
+// whole cache lines (8-byte stores straight from the MFMA's result, each
+// lane's piece of a token, measured slower). NR = n partials per token (1: copied, 2: merged); a tile has 16 /
+// NR tokens, so a wave owns 2 / NR tokens and 2 partial rows of every tile
+// either way. Same arithmetic and order of summation as the other kernels.
+constexpr int STREAM_NBUF = 3;  // tiles in LDS (rows, codes, staged output): the one being merged and two in flight
 
 template <int NR>
 struct StreamTile {
-  static constexpr int TT = TILE_T / NR;          // tokens per tile
-  static constexpr int TPW = TT / WAVES;          // tokens per wave
-  static constexpr int ROWS = 0;                  // rows: token slot tt, partial j at (tt NR + j) KiB
-  static constexpr int GATE = TILE_T * KVL * 2;   // gate rows: slot tt at GATE + 256 tt (head h's 128)
-  static constexpr int LSE = GATE + TT * VD * 2;  // LSEs: wave w's load at LSE + 256 w
-  static constexpr int BYTES = LSE + WAVES * LDS_WAVE_LSE;
-  static constexpr int LOADS = NR * TPW + TPW + 1;  // loads a wave issues per tile
+  static constexpr int TT = TILE_T / NR;      // tokens per tile
+  static constexpr int TPW = TT / WAVES;      // tokens per wave
+  static constexpr int BYTES = TILE_T * KVL * 2;  // rows: token slot tt, partial j at (tt NR + j) KiB
+  static constexpr int LOADS = NR * TPW + 2;  // loads a wave issues per tile: its rows, gate values, LSEs
+};
+
+// One tile's values that travel in registers: the gate values of this
+// lane's four output elements and, in lanes 0 and 1, one LSE each.
+struct StreamRegs {
+  v2u g;
+  float l;
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -1023,7 +1030,7 @@ struct StreamAddr {
   int o_stb, l_st4;       // bytes per token
   int lse_tail;           // LSE bytes a token's loads span
   uint32_t vrow[2];       // this lane's offset in the wave's k-th token's row
-  uint32_t vgate[2];      // .. in its gate row
+  uint32_t vgate;         // .. of its 4 gate values (token slot lane & 15, the MFMA output's rows)
   uint32_t vlse;          // .. among the LSEs
   uint32_t vout;          // this thread's piece of a staged output tile in core
 };
@@ -1044,8 +1051,8 @@ __device__ __forceinline__ StreamAddr stream_addr(const KArgs& a, int h, int wav
   for (int k = 0; k < 2; ++k) {
     const int tt = wave * L::TPW + (k < L::TPW ? k : 0);
     s.vrow[k] = (uint32_t)(tt * s.o_stb + lane * 16);
-    s.vgate[k] = (uint32_t)(tt * GROWS * 2 + lane * 4);
   }
+  s.vgate = (uint32_t)((lane & 15) * GROWS * 2 + (wave * 16 + (lane >> 4) * 4) * 2);
   // LSEs, 4 B a lane: with two partials lane j takes partial min(j, 1) of
   // the wave's token; with one, lane 0 the LSE of the wave's first token and
   // the other lanes that of its second
@@ -1060,19 +1067,21 @@ __device__ __forceinline__ StreamAddr stream_addr(const KArgs& a, int h, int wav
   return s;
 }
 
-// The loads of the tile [t0, tend) into its LDS buffer: every wave issues
-// exactly StreamTile<NR>::LOADS of them, for every tile index, also past its
-// last tile, so the number in flight is fixed. The rows and LSEs of tokens
-// past tend or the batch end, and the gate rows of tokens past tend, lie
-// beyond the end of their buffer resource (each token's bytes start past the
-// previous token's end): nothing is read, and what the LDS then holds is
-// never used. Without LSEs the LSE resource has zero bytes.
+// The loads of the tile [t0, tend): its rows into its LDS buffer
+// (stream_rows), then its gate values and LSEs into the registers returned
+// (stream_regs), with no other vector memory operation between the two.
+// Every wave issues exactly StreamTile<NR>::LOADS of them, for every tile
+// index, also past its last tile, so the number in flight is fixed. The
+// rows and LSEs of tokens past tend or the batch end, and the gate values of
+// tokens past tend, lie beyond the end of their buffer resource (each
+// token's bytes start past the previous token's end): nothing is read, the
+// registers get zeros and what the LDS then holds is never used. Without
+// LSEs the LSE resource has zero bytes.
 template <int NR>
-__device__ __forceinline__ void stream_issue(const KArgs& a, const StreamAddr& s, int t0, int tend, int batch_end,
-                                             int wave, uint8_t* buf) {
+__device__ __forceinline__ void stream_rows(const StreamAddr& s, int t0, int tend, int batch_end, int wave,
+                                            uint8_t* buf) {
   using L = StreamTile<NR>;
-  const int live = max(0, tend - t0);                 // tokens of the tile
-  const int use = max(0, min(tend, batch_end) - t0);  // .. with partials to read
+  const int use = max(0, min(tend, batch_end) - t0);  // tokens with partials to read
   const uint64_t orow = (uint64_t)(uint32_t)t0 * (uint32_t)s.o_stb;
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
@@ -1080,25 +1089,31 @@ __device__ __forceinline__ void stream_issue(const KArgs& a, const StreamAddr& s
         const_cast<uint8_t*>(s.o_h[j] + orow), (short)0, use ? (use - 1) * s.o_stb + KVL * 2 : 0, BUF_WORD3);
 #pragma unroll
     for (int k = 0; k < L::TPW; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + L::ROWS + ((wave * L::TPW + k) * NR + j) * KVL * 2),
-                                               16, s.vrow[k], 0, 0, NT_ROWS ? 2 : 0);  // 2: nt
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + ((wave * L::TPW + k) * NR + j) * KVL * 2), 16,
+                                               s.vrow[k], 0, 0, NT_ROWS ? 2 : 0);  // 2: nt
   }
+}
+
+template <int NR>
+__device__ __forceinline__ StreamRegs stream_regs(const KArgs& a, const StreamAddr& s, int t0, int tend,
+                                                  int batch_end) {
+  const int live = max(0, tend - t0);                 // tokens of the tile
+  const int use = max(0, min(tend, batch_end) - t0);  // .. with partials to read
+  StreamRegs out;
   {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(s.g_h + (uint64_t)(uint32_t)t0 * (GROWS * 2)), (short)0,
         live ? (live - 1) * (GROWS * 2) + VD * 2 : 0, BUF_WORD3);
-#pragma unroll
-    for (int k = 0; k < L::TPW; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + L::GATE + (wave * L::TPW + k) * VD * 2), 4,
-                                               s.vgate[k], 0, 0, 2);
+    out.g = (v2u)__builtin_amdgcn_raw_buffer_load_b64(r, s.vgate, 0, 0);
   }
   {
     const bool have = a.lse != nullptr && use > 0;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(s.l_h + (a.lse ? (uint64_t)(uint32_t)t0 * (uint32_t)s.l_st4 : 0)), (short)0,
         have ? (use - 1) * s.l_st4 + s.lse_tail : 0, BUF_WORD3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + L::LSE + wave * LDS_WAVE_LSE), 4, s.vlse, 0, 0, 0);
+    out.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, s.vlse, 0, 0));
   }
+  return out;
 }
 
 // The merge weights of two partials from their raw LSEs (wave-uniform), as
@@ -1139,104 +1154,136 @@ __device__ __forceinline__ uint4 stream_flush(const StreamAddr& s, int t0, int t
   return v;
 }
 
-// One tile of the streaming kernel: tile `it` is in LDS buffer `cur`; the
-// loads of tile it + 2 go to buffer `ahead` (the one tile it - 1 used); the
-// output staged for tile it - 1 (tokens p0 .. pend) is written first, and
-// this tile's goes to s_out. The three buffers are distinct LDS variables,
-// named at compile time in each step: the compiler then knows that reading
-// `cur` does not touch what the loads in flight write (`ahead` and the third
-// buffer), and leaves them in flight instead of waiting for all of them
-// before the first read.
+// The wave's issue priority (s_setprio takes an immediate). Two workgroups
+// share a CU; at equal priority the older one's waves issue first, so it
+// runs ahead and the younger one finishes alone, later. The streaming kernel
+// sets priority 3, 2, 1, 0 at tiles 0, 1, 2, 3 (mod 4): a workgroup one to
+// three tiles behind the other then has the higher priority at most tiles,
+// which keeps the two together (measured: two partials at S = 16384, 90.8
+// -> 86.0 us; one partial unchanged).
+__device__ __forceinline__ void issue_priority(int p) {
+  switch (p) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0);
+  }
+}
+
+// One tile of the streaming kernel, tile `it`. Its rows are in LDS buffer
+// `rows` (each wave loads and merges only its own tokens' rows there), its
+// gate values and LSEs in `regs`. The wave merges its tokens into the code
+// buffer (codes, scales), issues tile it + NBUF's rows into its part of
+// `rows`, and meets the other waves at the one barrier of the tile: then
+// every token's codes are complete and every wave is done with tile it - 1
+// (its MFMAs read the other code buffer, and the output tile staged for it,
+// out_prev, is written now). The MFMAs' result, times the gate, is staged
+// in out_cur; then tile it + NBUF's gate values and LSEs go to `regs` (a
+// register reloaded while its old value is still needed would be copied at
+// the loop's back edge, which waits for the load). The buffers are distinct
+// LDS variables named at compile time at each step: the compiler then knows
+// that reading one does not touch what the loads in flight write to the
+// others, and leaves those in flight.
 template <bool COPY, int NR>
 __device__ __forceinline__ void stream_step(const KArgs& a, const TileSched& ts, int it, int h, int wave, int lane,
                                             int batch_end, const StreamAddr& sad, const uint4 wv[4], int sa,
-                                            const uint8_t* cur, uint8_t* ahead, uint8_t* s_codes, uint8_t* s_scales,
-                                            uint8_t* s_out, int& p0, int& pend) {
+                                            uint8_t* rows, StreamRegs& regs, uint8_t* codes, uint8_t* scales,
+                                            uint8_t* out_cur, const uint8_t* out_prev, int& p0, int& pend) {
   using L = StreamTile<NR>;
   constexpr int TT = L::TT;
   const int tl = lane & 15;
   const int kb = lane >> 4;
-  // Tile it has landed when at most tile it + 1's loads are outstanding
-  // (loads complete in order, and a step's core stores come before the loads
-  // it issues); after the barrier every wave's share of it has, and every
-  // wave is done with tile it - 1: the codes and the staged output.
-  __builtin_amdgcn_s_waitcnt(wait_vm(L::LOADS));
-  lds_barrier();
-  const uint4 flushed = stream_flush<TT>(sad, p0, pend, s_out);
+  issue_priority(3 - (it & 3));
+  // This wave's share of tile it has landed when at most the loads of the
+  // tiles issued after it are outstanding (loads complete in order).
+  __builtin_amdgcn_s_waitcnt(wait_vm((STREAM_NBUF - 1) * L::LOADS));
   int t0, tend;
   tile_span<TT>(ts, it, t0, tend);
+  // lanes 0 and 1: the LSEs of the wave's two tokens (one partial) or of
+  // its token's two partials
+  const float l0 = lane_f(regs.l, 0), l1 = lane_f(regs.l, 1);
   // ---- merge (or copy) + quantise this wave's tokens
 #pragma unroll
   for (int k = 0; k < L::TPW; ++k) {
     const int tt = wave * L::TPW + k;
     const int t = t0 + tt;
     const bool live = t < tend, empty = t >= batch_end;
-    const uint4 v0 = *reinterpret_cast<const uint4*>(cur + L::ROWS + tt * NR * KVL * 2 + lane * 16);
-    // lanes 0 and 1 of the wave's LSE load: the LSEs of its tokens (one
-    // partial) or of its token's two partials
-    const float2 l2 = *reinterpret_cast<const float2*>(cur + L::LSE + wave * LDS_WAVE_LSE);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(rows + tt * NR * KVL * 2 + lane * 16);
     if constexpr (COPY) {
-      copy_stage(a, t, tt, h, lane, live, empty, v0, k ? l2.y : l2.x, s_codes, s_scales);
+      copy_stage(a, t, tt, h, lane, live, empty, v0, k ? l1 : l0, codes, scales);
     } else {
-      const uint4 v1 = *reinterpret_cast<const uint4*>(cur + L::ROWS + (tt * NR + 1) * KVL * 2 + lane * 16);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(rows + (tt * NR + 1) * KVL * 2 + lane * 16);
       uint32_t lat[4] = {0u, 0u, 0u, 0u};
       if (live && !empty) {
         int w0, w1;
-        two_weights(l2.x, l2.y, w0, w1);
+        two_weights(l0, l1, w0, w1);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (w0 & 0x7FFFFFFF) fma_row(__int_as_float(w0), v0, acc);
         if (w1 & 0x7FFFFFFF) fma_row(__int_as_float(w1), v1, acc);
 #pragma unroll
         for (int q = 0; q < 4; ++q) lat[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
       }
-      quant_to_lds(a, t, tt, h, lane, live, lat, s_codes, s_scales);
+      quant_to_lds(a, t, tt, h, lane, live, lat, codes, scales);
     }
   }
-  lds_barrier();  // the codes are complete; every wave is done with s_out and tile it - 1's buffer
-  // Tile it + 2's loads go out now, after the merge: the scalar work of
-  // forming them overlaps the MFMAs below instead of delaying the merge.
-  {
-    int n0, nend;
-    tile_span<TT>(ts, it + STREAM_NBUF - 1, n0, nend);
-    stream_issue<NR>(a, sad, n0, nend, batch_end, wave, ahead);
-  }
+  // the wave's rows of tile it are read (their values are used above): its
+  // part of the buffer takes tile it + NBUF's rows
+  int n0, nend;
+  tile_span<TT>(ts, it + STREAM_NBUF, n0, nend);
+  stream_rows<NR>(sad, n0, nend, batch_end, wave, rows);
+  lds_barrier();  // every token's codes are complete; every wave is done with tile it - 1
+  const uint4 kept = stream_flush<TT>(sad, p0, pend, out_prev);
 
-  // ---- W_UV, gate, stage: the lane holds rows v0..v0+3 (v0 = 16 wave +
-  // 4 kb) of token slot tl; its gate values come from the tile's LDS buffer
-  // (slots past an 8-token tile read bytes that are never stored)
-  const int sb = *reinterpret_cast<const int*>(s_scales + tl * NBLK + kb * 4);
+  // ---- W_UV, gate: the lane holds rows v0..v0+3 (v0 = 16 wave + 4 kb) of
+  // token slot tl (slots past an 8-token tile have gate values 0 and are
+  // never stored)
+  const int sb = *reinterpret_cast<const int*>(scales + tl * NBLK + kb * 4);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   {
-    const uint8_t* brow = s_codes + tl * 16;
+    const uint8_t* brow = codes + tl * 16;
     acc = mfma_step<0>(wv[0], *reinterpret_cast<const uint4*>(brow + (0 * 4 + kb) * CODE_ROW), acc, sa, sb);
     acc = mfma_step<1>(wv[1], *reinterpret_cast<const uint4*>(brow + (1 * 4 + kb) * CODE_ROW), acc, sa, sb);
     acc = mfma_step<2>(wv[2], *reinterpret_cast<const uint4*>(brow + (2 * 4 + kb) * CODE_ROW), acc, sa, sb);
     acc = mfma_step<3>(wv[3], *reinterpret_cast<const uint4*>(brow + (3 * 4 + kb) * CODE_ROW), acc, sa, sb);
   }
-  // stored unconditionally before any lane-dependent branch: the MFMAs run
-  // with the whole wave active
-  const uint2 g4 = *reinterpret_cast<const uint2*>(cur + L::GATE + tl * VD * 2 + (wave * 16 + kb * 4) * 2);
+  // computed and written by every lane, before any lane-dependent branch:
+  // the MFMAs run with the whole wave active
   const uint2 ab = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
-  *reinterpret_cast<uint2*>(s_out + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) =
-      make_uint2(pack_bf16(bf_lo(ab.x) * bf_lo(g4.x), bf_hi(ab.x) * bf_hi(g4.x)),
-                 pack_bf16(bf_lo(ab.y) * bf_lo(g4.y), bf_hi(ab.y) * bf_hi(g4.y)));
+  const uint2 cv = make_uint2(pack_bf16(bf_lo(ab.x) * bf_lo(regs.g.x), bf_hi(ab.x) * bf_hi(regs.g.x)),
+                              pack_bf16(bf_lo(ab.y) * bf_lo(regs.g.y), bf_hi(ab.y) * bf_hi(regs.g.y)));
+  *reinterpret_cast<uint2*>(out_cur + tl * OUT_ROW + (wave * 16 + kb * 4) * 2) = cv;
+  regs = stream_regs<NR>(a, sad, n0, nend, batch_end);
   p0 = t0;
   pend = tend;
-  asm volatile("" ::"v"(flushed.x), "v"(flushed.y), "v"(flushed.z), "v"(flushed.w));
+  // the stored values stay live until here, after the tile's other memory
+  // operations: their registers are not reused while the store may still
+  // read them, which would make the compiler wait for every load in flight
+  asm volatile("" ::"v"(kept.x), "v"(kept.y), "v"(kept.z), "v"(kept.w));
 }
+
+// Step I on the buffers of tile slot B (rows, registers RG, codes, output),
+// the previous tile's output in slot P.
+#define STREAM_STEP(I, B, RG, P)                                                                                \
+  stream_step<COPY, NR>(a, ts, I, h, wave, lane, batch_end, sad, wv, sa, s_buf##B, RG, s_codes##B, s_scales##B, \
+                        s_out##B, s_out##P, p0, pend)
 
 template <bool COPY, int NR>
 __global__ __launch_bounds__(THREADS) void mla_post_stream_kernel(const KArgs a, int wg_per_head) {
   static_assert(COPY == (NR == 1), "one partial is copied, two are merged");
-  static_assert(STREAM_NBUF == 3, "the tile loop names three buffers");
   using L = StreamTile<NR>;
   constexpr int TT = L::TT;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf0[L::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_buf1[L::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_buf2[L::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[LDS_CODES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[LDS_SCALES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_out[LDS_OUT];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes0[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes1[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes2[LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales0[LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales1[LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales2[LDS_SCALES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out0[LDS_OUT];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out1[LDS_OUT];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out2[LDS_OUT];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1250,35 +1297,55 @@ __global__ __launch_bounds__(THREADS) void mla_post_stream_kernel(const KArgs a,
   int sa = 0;
   load_wv(a, h, wave, lane & 15, lane >> 4, wv, sa);
   const StreamAddr sad = stream_addr<NR>(a, h, wave, lane);
+  StreamRegs r0, r1, r2;
   {
     int t0, tend;
     tile_span<TT>(ts, 0, t0, tend);
-    stream_issue<NR>(a, sad, t0, tend, batch_end, wave, s_buf0);
+    stream_rows<NR>(sad, t0, tend, batch_end, wave, s_buf0);
+    r0 = stream_regs<NR>(a, sad, t0, tend, batch_end);
     tile_span<TT>(ts, 1, t0, tend);
-    stream_issue<NR>(a, sad, t0, tend, batch_end, wave, s_buf1);
+    stream_rows<NR>(sad, t0, tend, batch_end, wave, s_buf1);
+    r1 = stream_regs<NR>(a, sad, t0, tend, batch_end);
+    tile_span<TT>(ts, 2, t0, tend);
+    stream_rows<NR>(sad, t0, tend, batch_end, wave, s_buf2);
+    r2 = stream_regs<NR>(a, sad, t0, tend, batch_end);
   }
   // 8-token tiles: MFMA columns 8..15 never hold a token, zero codes once
-  if constexpr (TT < TILE_T) empty_slot(a, TT + wave, h, lane, s_codes, s_scales);
+  if constexpr (TT < TILE_T) {
+    empty_slot(a, TT + wave, h, lane, s_codes0, s_scales0);
+    empty_slot(a, TT + wave, h, lane, s_codes1, s_scales1);
+    empty_slot(a, TT + wave, h, lane, s_codes2, s_scales2);
+  }
 
   int p0 = a.S, pend = a.S;  // tokens of the tile whose output is staged
+  // Whole rounds of three tiles, then the last one or two, with no exit from
+  // the middle of a round: an early exit would give the compiler a path from
+  // inside the round back to its start, along which it would count the
+  // latest loads as just issued and wait for them.
+  int it = 0;
 #pragma unroll 1
-  for (int it = 0; it < ts.count; it += STREAM_NBUF) {
-    stream_step<COPY, NR>(a, ts, it, h, wave, lane, batch_end, sad, wv, sa, s_buf0, s_buf2, s_codes, s_scales, s_out,
-                          p0, pend);
-    if (it + 1 >= ts.count) break;
-    stream_step<COPY, NR>(a, ts, it + 1, h, wave, lane, batch_end, sad, wv, sa, s_buf1, s_buf0, s_codes, s_scales,
-                          s_out, p0, pend);
-    if (it + 2 >= ts.count) break;
-    stream_step<COPY, NR>(a, ts, it + 2, h, wave, lane, batch_end, sad, wv, sa, s_buf2, s_buf1, s_codes, s_scales,
-                          s_out, p0, pend);
+  for (; it + 3 <= ts.count; it += 3) {
+    STREAM_STEP(it, 0, r0, 2);
+    STREAM_STEP(it + 1, 1, r1, 0);
+    STREAM_STEP(it + 2, 2, r2, 1);
+  }
+  const uint8_t* last = s_out2;
+  if (it < ts.count) {
+    STREAM_STEP(it, 0, r0, 2);
+    last = s_out0;
+    if (it + 1 < ts.count) {
+      STREAM_STEP(it + 1, 1, r1, 0);
+      last = s_out1;
+    }
   }
   lds_barrier();
-  stream_flush<TT>(sad, p0, pend, s_out);
+  stream_flush<TT>(sad, p0, pend, last);
   // the loads issued for tile indices past the last are still in flight:
   // they read nothing, but the wave waits for them (and its stores) before
   // it ends
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 }
+#undef STREAM_STEP
 
 // ---------------------------------------------------------------- stand-alone quantiser
 
