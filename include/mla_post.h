@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MLA_POST_VERSION 4
+#define MLA_POST_VERSION 5
 
 /* Fixed shapes (the page's per-rank Kimi-K3 shapes at 8-way tensor parallelism). */
 #define MLA_POST_HEADS 12   /* local heads */
@@ -146,8 +146,8 @@ int mla_post_check(const mla_post_args* a);
 #define MLA_POST_KERNEL_SPLIT_ROWS 3 /* one small token tile per workgroup, 8 / tile_tokens waves sharing the
                                         partials of each token (many partials, few tokens) */
 #define MLA_POST_KERNEL_STREAM 4     /* since version 4: workgroups that each keep one head and walk its tiles,
-                                        loading two tiles ahead straight into LDS (one or two partials, many
-                                        tokens) */
+                                        loading each tile's rows two tiles ahead straight into LDS (one or
+                                        two partials, many tokens); since version 5 two per CU */
 
 typedef struct mla_post_plan {
   int32_t kernel;              /* MLA_POST_KERNEL_* */
@@ -158,9 +158,13 @@ typedef struct mla_post_plan {
                                   kernel: n; else 0 */
   int32_t lse_chunks;          /* persistent and split-rows kernels: 64-lane chunks of partials per token
                                   (1, 2, 4 or 8); else 1 */
-  int32_t workgroups_per_head; /* the grid is 12 times this */
+  int32_t workgroups_per_head; /* the grid is 12 times this, except for the streaming kernel (since version
+                                  5): its grid is `workgroups`, workgroup b taking head b mod 12; heads
+                                  h < workgroups mod 12 have workgroups_per_head workgroups, the others
+                                  one fewer */
   int32_t workgroups;          /* grid size (workgroups of 512 threads) */
-  int32_t full_tiles;          /* persistent and streaming kernels: full tiles of every workgroup */
+  int32_t full_tiles;          /* persistent and streaming kernels: full tiles of every workgroup (streaming
+                                  kernel: of a head with workgroups_per_head workgroups) */
   int32_t short_tokens;        /* persistent and streaming kernels: tokens of one more, shorter tile per
                                   workgroup (at most tile_tokens; the last workgroups of a head may get
                                   fewer or none); 0: none */

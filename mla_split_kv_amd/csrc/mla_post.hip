@@ -1268,7 +1268,7 @@ __device__ __forceinline__ void stream_step(const KArgs& a, const TileSched& ts,
                         s_out##B, s_out##P, p0, pend)
 
 template <bool COPY, int NR>
-__global__ __launch_bounds__(THREADS) void mla_post_stream_kernel(const KArgs a, int wg_per_head) {
+__global__ __launch_bounds__(THREADS) void mla_post_stream_kernel(const KArgs a) {
   static_assert(COPY == (NR == 1), "one partial is copied, two are merged");
   using L = StreamTile<NR>;
   constexpr int TT = L::TT;
@@ -1287,9 +1287,10 @@ __global__ __launch_bounds__(THREADS) void mla_post_stream_kernel(const KArgs a,
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int h, slot;
-  head_and_slot(h, slot);
-  const TileSched ts = tile_sched<TT>(a.S, wg_per_head, slot, true);
+  // workgroup b: head b mod 12, slot b / 12 of that head's k workgroups
+  const int h = blockIdx.x % NH, slot = blockIdx.x / NH;
+  const int k = gridDim.x / NH + (h < (int)(gridDim.x % NH) ? 1 : 0);
+  const TileSched ts = tile_sched<TT>(a.S, k, slot, true);
   const int batch_end = a.qsl ? a.qsl[a.S / a.q] : a.S;
 
   // W_V[h] first (the first MFMAs wait for it anyway), then the first tiles
@@ -1564,12 +1565,14 @@ int split_tile(int n, int S, int cus) {
 // with LSEs; the split-rows kernel for many partials and few tokens; else
 // the persistent kernel. One partial is copied. mla_post launches exactly
 // this.
-// Workgroups per head of the streaming kernel: as many as are resident at
-// once (its LDS ring and buffers: 2 per CU with three tile buffers, 3 with
-// two), rounded down to a multiple of 8 so that the 12 heads of a slot share
-// an XCD (40 or 64 at 256 CUs).
+// Workgroups of the streaming kernel: as many as are resident at once, two
+// per CU (its LDS), so that every CU holds two: workgroup b takes head
+// b mod 12, and heads below (workgroups mod 12) get one workgroup more than
+// the others (43 and 42 at 256 CUs). A grid of whole rounds of 12 (40 per
+// head) left 32 of 256 CUs with one workgroup, which finished early and then
+// idled (512 workgroups: 3-5% faster at S = 4096..16384).
 constexpr int STREAM_WG_PER_CU = 2;
-int stream_workgroups_per_head(int cus) { return max(XCDS, (STREAM_WG_PER_CU * cus / NH) / XCDS * XCDS); }
+int stream_workgroups(int cus) { return max(NH, STREAM_WG_PER_CU * cus); }
 
 // Whether the streaming kernel takes the call: one or two partials, no KV
 // length masks, a layout where rows and LSEs move by a fixed stride per token
@@ -1601,8 +1604,8 @@ mla_post_plan make_plan(const mla_post_args* a, int cus) {
     p.tile_tokens = tt;
     p.rows_held = a->n;
     p.lse_chunks = 1;
-    p.workgroups_per_head = stream_workgroups_per_head(cus);
-    p.workgroups = NH * p.workgroups_per_head;
+    p.workgroups = stream_workgroups(cus);
+    p.workgroups_per_head = (p.workgroups + NH - 1) / NH;
     if (tt == TILE_T)
       tile_counts<TILE_T>(a->S, p.workgroups_per_head, true, p.full_tiles, p.short_tokens);
     else
@@ -1719,8 +1722,8 @@ int launch_plan(const KArgs& k, const mla_post_plan& p, bool copy, hipStream_t s
   const dim3 grid((unsigned)p.workgroups), block(THREADS);
   const int wph = p.workgroups_per_head;
   if (p.kernel == MLA_POST_KERNEL_STREAM)
-    return copy ? launch(mla_post_stream_kernel<true, 1>, grid, block, stream, k, wph)
-                : launch(mla_post_stream_kernel<false, 2>, grid, block, stream, k, wph);
+    return copy ? launch(mla_post_stream_kernel<true, 1>, grid, block, stream, k)
+                : launch(mla_post_stream_kernel<false, 2>, grid, block, stream, k);
   if (copy) return launch(mla_post_kernel<true, 1, 0>, grid, block, stream, k, wph);
   if (p.pair_rows == PF_ROWS / 2) return launch(mla_post_kernel<false, 1, PF_ROWS / 2>, grid, block, stream, k, wph);
   if (p.lse_chunks == 1) return launch(mla_post_kernel<false, 1, 0>, grid, block, stream, k, wph);

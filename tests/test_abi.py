@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.mla_post_version() == 4
+    assert lib.mla_post_version() == 5
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.mla_post_strerror(st).decode()
     assert lib.mla_post_strerror(-99).decode() == "unknown status"

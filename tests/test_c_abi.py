@@ -95,7 +95,7 @@ def test_plan_from_c(probe_output):
 
 def test_versions_agree(probe_output):
     sizes, _, _ = probe_output
-    assert sizes["header_version"] == sizes["library_version"] == 4
+    assert sizes["header_version"] == sizes["library_version"] == 5
 
 
 def test_status_codes_from_c(probe_output):

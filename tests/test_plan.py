@@ -72,23 +72,24 @@ TABLE = [
     ((4, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=4)),
     # two partials with LSEs: the one-tile instance below 6 tokens per CU
     # (S = 1536 at 256 CUs), the streaming kernel from there (8-token tiles,
-    # 40 workgroups per head, leftover tokens dealt out evenly)
+    # 2 workgroups per CU: 43 for heads 0..7, 42 for heads 8..11, leftover
+    # tokens dealt out evenly)
     ((2, 1535, True), dict(kernel="one_tile", tile_tokens=16, rows_held=2, workgroups_per_head=96)),
-    ((2, 1536, True), dict(kernel="stream", tile_tokens=8, rows_held=2, workgroups_per_head=40, workgroups=480,
-                           full_tiles=4, short_tokens=7)),
-    ((2, 8200, True), dict(kernel="stream", tile_tokens=8, rows_held=2, workgroups_per_head=40, full_tiles=25,
-                           short_tokens=5)),
-    ((2, 1 << 20, True), dict(kernel="stream", tile_tokens=8, workgroups_per_head=40)),
+    ((2, 1536, True), dict(kernel="stream", tile_tokens=8, rows_held=2, workgroups_per_head=43, workgroups=512,
+                           full_tiles=4, short_tokens=4)),
+    ((2, 8200, True), dict(kernel="stream", tile_tokens=8, rows_held=2, workgroups_per_head=43, full_tiles=23,
+                           short_tokens=7)),
+    ((2, 1 << 20, True), dict(kernel="stream", tile_tokens=8, workgroups_per_head=43, workgroups=512)),
     # one partial, with an LSE or not, is copied: the one-tile instance while
     # it fits, the persistent kernel up to 6 tokens per CU, then the
     # streaming kernel (16-token tiles)
     ((1, 1535, True), dict(kernel="persistent", workgroups_per_head=40, pair_rows=0)),
-    ((1, 1536, True), dict(kernel="stream", tile_tokens=16, rows_held=1, workgroups_per_head=40, full_tiles=2,
-                           short_tokens=7)),
-    ((1, 4096, True), dict(kernel="stream", tile_tokens=16, rows_held=1, workgroups_per_head=40, full_tiles=6,
-                           short_tokens=7)),
+    ((1, 1536, True), dict(kernel="stream", tile_tokens=16, rows_held=1, workgroups_per_head=43, full_tiles=2,
+                           short_tokens=4)),
+    ((1, 4096, True), dict(kernel="stream", tile_tokens=16, rows_held=1, workgroups_per_head=43, full_tiles=5,
+                           short_tokens=16)),
     ((1, 4096, False), dict(kernel="stream", tile_tokens=16, rows_held=1)),
-    ((1, 1 << 20, True), dict(kernel="stream", workgroups_per_head=40)),
+    ((1, 1 << 20, True), dict(kernel="stream", workgroups_per_head=43)),
     ((5, 2048, True), dict(kernel="persistent", workgroups_per_head=64, pair_rows=0)),
     # the one-round rule (65 to 96 tiles) and the leftover deal
     ((16, 1100, True), dict(kernel="persistent", workgroups_per_head=40, workgroups=480, full_tiles=1, short_tokens=12)),
@@ -153,7 +154,7 @@ def test_routing_table_at_256_cus(key, expect):
         assert p["workgroups"] == 12 * p["workgroups_per_head"]
     elif p["kernel"] == "stream":
         assert p["tile_tokens"] == 16 // key[0] and p["rows_held"] == key[0] and p["pair_rows"] == 0
-        assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["workgroups_per_head"] % 8 == 0
+        assert p["workgroups"] == 2 * p["cus"] and p["workgroups_per_head"] == -(-p["workgroups"] // 12)
     else:
         assert p["tile_tokens"] == 16 and p["rows_held"] == 0
         assert p["pair_rows"] == (4 if key[2] and 2 <= key[0] <= 4 else 0)
@@ -173,12 +174,26 @@ def test_invalid_arguments_give_the_check_status():
     assert lib.mla_post_plan_for(ctypes.byref(args(4, 8)), 256, None) == -1
 
 
-def covered(p, S):
+def schedule(S, k, tt):
+    """The schedule rule for k workgroups of a head: full tiles of tt tokens
+    at stride k, then the leftover tokens dealt out evenly (runs of
+    ceil(rest / k)): (full tiles, short tokens)."""
+    main = S // (tt * k)
+    rest = S - main * tt * k
+    return main, -(-rest // k)
+
+
+def covered(p, S, k=None):
     """Token -> number of persistent or streaming workgroups of one head that
     own it, from the plan's fields and the schedule rule (full tiles at
     stride k, then the leftover tokens in consecutive runs of short_tokens,
-    slot by slot)."""
-    k, main, chunk, tt = p["workgroups_per_head"], p["full_tiles"], p["short_tokens"], p["tile_tokens"]
+    slot by slot). k: a streaming head's own workgroup count, when it differs
+    from workgroups_per_head (its tiles then follow the same rule)."""
+    k0, main, chunk, tt = p["workgroups_per_head"], p["full_tiles"], p["short_tokens"], p["tile_tokens"]
+    if k is None or k == k0:
+        k = k0
+    else:
+        main, chunk = schedule(S, k, tt)
     count = np.zeros(S, dtype=np.int64)
     for slot in range(k):
         for i in range(main):
@@ -204,7 +219,20 @@ def test_schedule_covers_every_token_once(cus):
         for n, lse in ((1, False), (1, True), (2, True), (4, True), (6, True), (16, True), (20, True), (100, True),
                        (256, True)):
             p = plan(n, int(S), lse, cus)
-            assert p["workgroups"] == 12 * p["workgroups_per_head"] and p["cus"] == cus
+            assert p["cus"] == cus
+            if p["kernel"] == "stream":
+                # heads below workgroups mod 12 have workgroups_per_head
+                # workgroups, the others one fewer; each head's tokens are
+                # covered once either way
+                w, k = p["workgroups"], p["workgroups_per_head"]
+                assert w == 2 * cus and k == -(-w // 12)
+                assert (p["full_tiles"], p["short_tokens"]) == schedule(int(S), k, p["tile_tokens"])
+                assert 0 <= p["short_tokens"] <= p["tile_tokens"]
+                for kh in {w // 12 + (h < w % 12) for h in range(12)}:
+                    assert 0 <= schedule(int(S), kh, p["tile_tokens"])[1] <= p["tile_tokens"]
+                    assert np.all(covered(p, int(S), kh) == 1), (n, S, cus, kh, p)
+                continue
+            assert p["workgroups"] == 12 * p["workgroups_per_head"]
             if p["kernel"] in ("one_tile", "split_rows"):
                 assert p["workgroups_per_head"] * p["tile_tokens"] >= S > (p["workgroups_per_head"] - 1) * p["tile_tokens"]
                 continue
