@@ -25,15 +25,19 @@
  * partials (include/mla_post.h: merge, bf16 latents, MXFP4, W_UV, gate).
  *
  * The handoff is this library's own, not the page's: no workgroup ever
- * waits for another. Each (request, split) workgroup writes its partials to
- * the workspace with stores that go through to the device's coherence point
+ * waits for another. The launch has two workgroups per CU (fewer when there
+ * are fewer units); each takes (request, split) units in order, its first
+ * by its block index and each later one from a queue counter in the
+ * workspace (a vector atomic at device scope), until none is left, then
+ * counts itself out on a second counter; the last one out sets both back
+ * to 0. After a unit's attention the workgroup writes its partials to the
+ * workspace with stores that go through to the device's coherence point
  * (device-scope cache policy), waits for them to complete, then adds 1 to
- * its request's counter (a vector atomic at device scope); the workgroup
- * that brings the counter to n reads that request's partials with loads of
- * the same policy, merges them and runs W_UV for its tokens, then sets the
- * counter back to 0. So the launch cannot deadlock whatever order or
- * placement its workgroups get, and a call leaves the counters as it found
- * them.
+ * its request's counter; the workgroup that brings the counter to n reads
+ * that request's partials with loads of the same policy, merges them and
+ * runs W_UV for its tokens, then sets the counter back to 0. So the launch
+ * cannot deadlock whatever order or placement its workgroups get, and a
+ * call leaves the counters as it found them.
  *
  * Conventions as in mla_post.h (C linkage, caller-owned device memory,
  * asynchronous on the caller's stream, MLA_POST_* status codes, validation
@@ -75,7 +79,7 @@ typedef struct mla_decode_args {
 
   void* workspace;         /* device memory of mla_decode_workspace's size, 256-byte aligned; its
                               counters must be zero before the first call (mla_decode_workspace_init)
-                              and are zero again after every fused call */
+                              and are zero again after every call */
   int64_t workspace_bytes;
 
   /* optional stage outputs of the merge (NULL to skip), as mla_post's:
@@ -86,7 +90,8 @@ typedef struct mla_decode_args {
 } mla_decode_args;
 
 /* Workspace bytes for R requests of q tokens and n splits, and where its
- * parts start (byte offsets): counters int32 [R]; partials bf16
+ * parts start (byte offsets): counters int32 [R + 2] (one per request, then
+ * the unit queue's two); partials bf16
  * [R, n, q, 12, 512] (split j of token t = r q + tt, head h at row
  * ((r n + j) q + tt) 12 + h); LSEs float32 [R, n, q, 12] (same order).
  * After a call the partials and LSEs of that call stay there. Any output
@@ -94,9 +99,9 @@ typedef struct mla_decode_args {
 int mla_decode_workspace(int32_t R, int32_t q, int32_t n, int64_t* bytes, int64_t* off_counters,
                          int64_t* off_partials, int64_t* off_lse);
 
-/* Zero the workspace's counters (a small fill kernel on `stream`; no memset,
- * so it may be captured in a graph). Needed once, before the first fused
- * call on a new workspace. */
+/* Zero the workspace's R + 2 counters (a small fill kernel on `stream`; no
+ * memset, so it may be captured in a graph). Needed once, before the first
+ * call (mla_decode or mla_decode_partials) on a new workspace. */
 int mla_decode_workspace_init(void* workspace, int32_t R, void* stream);
 
 /* One launch: the split-KV attention of every (request, split) and, in the
@@ -104,7 +109,8 @@ int mla_decode_workspace_init(void* workspace, int32_t R, void* stream);
 int mla_decode(const mla_decode_args* a, void* stream);
 
 /* The attention alone: every (request, split) partial and LSE into the
- * workspace, nothing merged (counters untouched, core not written). With
+ * workspace, nothing merged (the request counters untouched, the queue's
+ * used and left at 0; core not written). With
  * mla_post on the workspace's partials (request-major: n = n, q = q,
  * o_sj = q*6144, o_sr = (n-1)*q*6144, o_st = 6144, o_sh = 512, and the same
  * strides over the LSEs divided by 512) it gives the same core as

@@ -534,8 +534,9 @@ class DecodeWorkspace:
         _raise(lib, lib.mla_decode_workspace_init(ctypes.c_void_p(self.mem.data_ptr()), self.R, ctypes.c_void_p(_stream(self.mem.device))))
 
     def counters(self):
+        """int32 [R + 2]: the request counters, then the unit queue's two."""
         c = self.layout["counters"]
-        return self.mem[c : c + 4 * self.R].view(torch.int32)
+        return self.mem[c : c + 4 * (self.R + 2)].view(torch.int32)
 
     def partials(self):
         """(o bf16 [R, n, q, 12, 512], lse float32 [R, n, q, 12]) views."""

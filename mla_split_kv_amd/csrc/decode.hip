@@ -41,6 +41,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "device.h"
@@ -71,7 +72,6 @@ constexpr int BLOCK_BYTES = TAIL + BC * TROW;  // one LDS block
 constexpr int LOADS_PER_WAVE = BC / DW + BC / 8 / DW;  // a wave's 16-byte-per-lane loads of one block
 constexpr int KSTEPS = DQK / 32;             // score MFMA steps over the 576 dims
 constexpr int NCOLT = KVL / 16;              // value column tiles (32)
-constexpr int XCDS = 8;
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 // consumer LDS (reuses the KV buffers): codes and scales of 12 heads, core rows
@@ -102,6 +102,17 @@ constexpr int CPOL_AGENT = 16;
 // outstanding; wait for every LDS operation.
 constexpr int WAITCNT_VM(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int WAITCNT_LGKM0 = 15 | (3 << 14) | (7 << 4);
+
+// A workgroup barrier for LDS hazards alone: the wave's LDS operations are
+// complete, then s_barrier (__syncthreads also waits for every vector memory
+// operation in flight). The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 struct DArgs {
   const uint8_t* qry;
@@ -150,7 +161,9 @@ __device__ __forceinline__ float xor_sum(float x) {
 // every run (the instruction cache holds the attention loop), which measured
 // several times slower than its memory round trips.
 __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  int tid = threadIdx.x;  // opaque, as in decode_unit
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t* s_codes = lds;                        // [12][LDS_CODES]
   uint8_t* s_scales = lds + NH * LDS_CODES;      // [12][16 slots][16 blocks]
@@ -297,25 +310,59 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
 
 // ---------------------------------------------------------------- the attention (and the fused launch)
 
-template <bool FUSED>
-__global__ __launch_bounds__(DTHREADS, 2) void mla_decode_kernel(const DArgs a) {
-  // One LDS variable (the flag below lives past the KV blocks): with a single
-  // one the compiler does not order this wave's LDS reads behind the
-  // buffer-to-LDS loads in flight, whose completion the block loop waits for
-  // itself; with several it treats every access to the KV array as touching
-  // the block being loaded.
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES + 16];
-  int* const s_last = reinterpret_cast<int*>(lds + LDS_BYTES);
+// One thread's atomic add of 1 at device scope, returning the old value.
+// The address is made a per-lane value, so the compiler issues the one
+// atomic as it stands instead of its wave-wide form, which takes the
+// returned value at once (a wait for the round trip where the atomic is
+// issued rather than where its value is used).
+__device__ __forceinline__ int count_in(int32_t* c) {
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  return __hip_atomic_fetch_add(c + zero, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63;
+// Thread 0's claim of the workgroup's next unit: the queue counter's old
+// value.
+__device__ __forceinline__ int claim_unit(int32_t* q_next) { return count_in(q_next); }
+
+// One unit: the attention of request r's split j (and, fused, the merge of
+// request r when this unit completes it). lds: the workgroup's LDS (KV
+// blocks, then the consumer's buffers); s_last, s_next: words past them.
+// Thread 0 claims the workgroup's next unit and puts the claim in s_next
+// before the unit's end. Attention alone: the claim is `next`, issued before
+// the unit's loads, and is stored once the KV loop has waited for every load
+// (so for the claim too). Fused: the claim goes out with the partial stores
+// (a claim held through the KV loop would take one of the registers the
+// loop has none left of), and the wait for the stores covers it.
+//
+// Handoff. The partials are written coherent at device scope (sc1,
+// write-through to the device's coherence point); every wave waits for its
+// stores to complete before the barrier that precedes the counter's atomic
+// add, as a device-scope release (a writeback of the whole L2, then the same
+// wait) would order them, without the writeback. The workgroup that brings
+// the counter to n merges the request at once (consume), reading the
+// partials with sc1 loads, which a stale line cannot satisfy, in place of a
+// device-scope acquire (an invalidation of the whole L2). (Counting a unit
+// in one unit later, after the next unit's KV loop has waited for its
+// stores, measured 5% slower: the merges then read partials written a unit
+// earlier, and took 10% longer.)
+template <bool FUSED>
+__device__ __forceinline__ void decode_unit(const DArgs& a, int r, int j, uint8_t* lds, int* s_last, int* s_next,
+                                            int32_t* q_next, int next) {
+  // the thread index as the compiler cannot tell from one unit to the next:
+  // values derived from it are then computed within the unit, not hoisted
+  // out of the unit loop and held (spilled) across it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // unit (request r, split j): request r's splits all on XCD r mod 8
-  const int xcd = blockIdx.x % XCDS, slot = blockIdx.x / XCDS;
-  const int r = XCDS * (slot / a.n) + xcd, j = slot % a.n;
-  if (r >= a.R) return;  // the whole workgroup: no barrier is pending
   const int qrows = NH * a.q;
-  const int base = a.indptr[r];
-  const int L = max(a.indptr[r + 1] - base, 0);
+  // indptr does not change during the launch: read through the constant
+  // address space, as scalar loads
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* ip = (const_i32*)(uintptr_t)a.indptr;
+  const int base = ip[r];
+  const int L = max(ip[r + 1] - base, 0);
   const int k0 = base + (int)((int64_t)j * L / a.n);
   const int nrows = base + (int)((int64_t)(j + 1) * L / a.n) - k0;
   const int nblk = (nrows + BC - 1) / BC;
@@ -506,21 +553,26 @@ __global__ __launch_bounds__(DTHREADS, 2) void mla_decode_kernel(const DArgs a) 
   if (nblk > 0) block(0);
 #pragma unroll 1
   for (int b = 1; b < nblk; ++b) block(b);
-  __syncthreads();
+  if constexpr (!FUSED) {
+    if (tid == 0) *s_next = next;
+  }
+  lds_barrier();  // every wave is done with the KV blocks
 
   // partials: bf16(O / sum) and ln(sum exp) of each query row (an empty split:
   // zeros and -inf). Each compute wave stages its 16 rows in LDS (the KV
   // blocks are free after the barrier above) and writes each row's 1 KiB as
   // one store of 16 bytes per lane: whole cache lines, since the partials are
   // written through to the device's coherence point (sc1).
+  uint8_t* ot = lds + wave * 16 * MROW;  // this wave's rows, MROW bytes apart
+  const bool any = nblk > 0;
   if (compute) {
-    uint8_t* ot = lds + wave * 16 * MROW;  // this wave's rows, MROW bytes apart
-    const bool any = nblk > 0;
     const float inv = any ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int c = 0; c < NCOLT; ++c)
       *reinterpret_cast<uint2*>(ot + c16 * MROW + (16 * c + 4 * g) * 2) =
           make_uint2(pack_bf16(acc[c][0] * inv, acc[c][1] * inv), pack_bf16(acc[c][2] * inv, acc[c][3] * inv));
+  }
+  if (compute) {
     const float lse = any ? (m2 + __log2f(lsum)) * LN2 : -INFINITY;
     __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this wave's rows are in LDS (the wave reads only its own)
     for (int i = 0; i < 16; ++i) {
@@ -537,23 +589,65 @@ __global__ __launch_bounds__(DTHREADS, 2) void mla_decode_kernel(const DArgs a) 
   }
 
   if constexpr (FUSED) {
-    // Handoff. The partials were written coherent at device scope (sc1,
-    // write-through to the device's coherence point); waiting for every
-    // store of this thread to complete before the barrier puts them there
-    // before the counter's atomic add, which a device-scope release (a
-    // writeback of the whole L2, then the same wait) would also do, at the
-    // cost of the writeback. The merging unit reads them with sc1 loads,
-    // which a stale line cannot satisfy, in place of a device-scope acquire
-    // (an invalidation of the whole L2).
+    // the claim of the next unit goes out with the partial stores; the wait
+    // for them covers it
+    if (tid == 0) next = claim_unit(q_next);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) *s_last = __hip_atomic_fetch_add(a.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.n - 1;
-    __syncthreads();
+    next = __builtin_amdgcn_readfirstlane(next);  // lane 0's (thread 0's) value, taken on every path
+    if (tid == 0) *s_next = next;
+    lds_barrier();  // every wave's partial stores are complete
+    if (tid == 0) *s_last = count_in(a.cnt + r) == a.n - 1;
+    lds_barrier();
     // the same value on every lane: read as a scalar, so the branch is uniform
     // and the consumer's MFMAs run with the whole wave active
-    if (!__builtin_amdgcn_readfirstlane(*s_last)) return;
-    consume(a, r, lds);
-    if (tid == 0) __hip_atomic_store(a.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(*s_last)) {
+      consume(a, r, lds);
+      if (tid == 0) __hip_atomic_store(a.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// The launch: DECODE_WG_PER_CU workgroups per CU (or one per unit, if fewer),
+// each taking units u = (request u / n, split u mod n) in order until none is
+// left: its first by its block index, each later one from the queue counter
+// (units gridDim.x, gridDim.x + 1, ..), claimed while the unit before it
+// runs, so the claim's round trip overlaps that unit. A request's splits
+// are consecutive units, so they run at about the same time and the merge
+// follows them closely. Units are not tied to XCDs or to dispatch order: a
+// grid of one workgroup per unit, dispatched in order to the XCDs in turn,
+// left slots idle on every XCD behind the one where merges held workgroups
+// longest (about 200 of 512 slots on average in the fused launch). A
+// workgroup with no unit left counts itself out; the last one sets both
+// counters back to zero for the next launch.
+template <bool FUSED>
+__global__ __launch_bounds__(DTHREADS, 2) void mla_decode_kernel(const DArgs a) {
+  // One LDS variable (the flag words below live past the KV blocks): with a
+  // single one the compiler does not order this wave's LDS reads behind the
+  // buffer-to-LDS loads in flight, whose completion the block loop waits for
+  // itself; with several it treats every access to the KV array as touching
+  // the block being loaded.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES + 16];
+  int* const s_last = reinterpret_cast<int*>(lds + LDS_BYTES);
+  int* const s_next = s_last + 1;
+  int32_t* const q_next = a.cnt + a.R;  // units handed out past the first gridDim.x
+  int32_t* const q_done = q_next + 1;   // workgroups with no unit left
+  const int units = a.R * a.n;
+  int u = blockIdx.x;
+  while (u < units) {
+    int next = 0;
+    if (!FUSED && threadIdx.x == 0) next = claim_unit(q_next);
+    decode_unit<FUSED>(a, u / a.n, u % a.n, lds, s_last, s_next, q_next, next);
+    // every wave is done with the unit's LDS before any starts the next (the
+    // attention's partial stores stay in flight)
+    lds_barrier();
+    u = (int)gridDim.x + __builtin_amdgcn_readfirstlane(*s_next);
+  }
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(q_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+    // every workgroup has made its last claim (each counts itself out after
+    // its claim has returned)
+    __hip_atomic_store(q_next, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -580,8 +674,8 @@ struct WsLayout {
 bool ws_layout(int64_t R, int64_t q, int64_t n, WsLayout* w) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t rows = R * n * q * NH;  // R <= 2^24, n <= 64, q <= 4: no overflow
-  w->cnt = 0;
-  w->part = up(R * 4);
+  w->cnt = 0;  // R request counters, then the unit queue's two
+  w->part = up((R + 2) * 4);
   w->lse = w->part + up(rows * KVL * 2);
   w->bytes = w->lse + up(rows * 4);
   return true;
@@ -614,7 +708,6 @@ int check(const mla_decode_args* a) {
   WsLayout w;
   ws_layout(a->R, a->q, a->n, &w);
   if (a->workspace_bytes < w.bytes) return MLA_POST_EINVAL;
-  if ((int64_t)XCDS * a->n * ((a->R + XCDS - 1) / XCDS) * DTHREADS >= (int64_t(1) << 32)) return MLA_POST_ERANGE;
   return MLA_POST_OK;
 }
 
@@ -673,13 +766,18 @@ void* scratch_on_device() {
   return p;
 }
 
+constexpr int DECODE_WG_PER_CU = 2;  // resident at once: two KV blocks of LDS each, 256 VGPRs
+
+unsigned decode_grid(const mla_decode_args* a) {
+  return (unsigned)std::min<int64_t>((int64_t)a->R * a->n, (int64_t)DECODE_WG_PER_CU * mla_dev::device_cus());
+}
+
 template <bool FUSED>
 int run(const mla_decode_args* a, void* stream) {
   const int st = check(a);
   if (st != MLA_POST_OK || a->R == 0) return st;
   const DArgs d = device_args(a);
-  const int64_t grid = (int64_t)XCDS * a->n * ((a->R + XCDS - 1) / XCDS);
-  return launch(mla_decode_kernel<FUSED>, dim3((unsigned)grid), dim3(DTHREADS), static_cast<hipStream_t>(stream), d);
+  return launch(mla_decode_kernel<FUSED>, dim3(decode_grid(a)), dim3(DTHREADS), static_cast<hipStream_t>(stream), d);
 }
 
 }  // namespace
@@ -704,8 +802,8 @@ int mla_decode_workspace_init(void* workspace, int32_t R, void* stream) {
   if (R == 0) return MLA_POST_OK;
   if (!workspace) return MLA_POST_EINVAL;
   if (!aligned(workspace, 256)) return MLA_POST_EALIGN;
-  return launch(zero_counters, dim3((unsigned)((R + 255) / 256)), dim3(256), static_cast<hipStream_t>(stream),
-                static_cast<int32_t*>(workspace), (int)R);
+  return launch(zero_counters, dim3((unsigned)((R + 2 + 255) / 256)), dim3(256), static_cast<hipStream_t>(stream),
+                static_cast<int32_t*>(workspace), (int)R + 2);
 }
 
 int mla_decode(const mla_decode_args* a, void* stream) { return run<true>(a, stream); }
@@ -735,11 +833,11 @@ int mla_decode_noalloc(const mla_decode_args* a, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // the counters must start at zero: a fill kernel (no memset, so the call
   // may be captured in a graph)
-  const int z = launch(zero_counters, dim3((unsigned)((a->R + 255) / 256)), dim3(256), s, static_cast<int32_t*>(p), (int)a->R);
+  const int z =
+      launch(zero_counters, dim3((unsigned)((a->R + 2 + 255) / 256)), dim3(256), s, static_cast<int32_t*>(p), (int)a->R + 2);
   if (z != MLA_POST_OK) return z;
   const DArgs d = device_args(&b);
-  const int64_t grid = (int64_t)XCDS * b.n * ((b.R + XCDS - 1) / XCDS);
-  return launch(mla_decode_kernel<true>, dim3((unsigned)grid), dim3(DTHREADS), s, d);
+  return launch(mla_decode_kernel<true>, dim3(decode_grid(&b)), dim3(DTHREADS), s, d);
 }
 
 }  // extern "C"

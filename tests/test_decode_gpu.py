@@ -10,7 +10,11 @@ Each case checks:
          mla_post oracle run on those same partials;
   the fused launch's core bit for bit against the unfused pair (the
   attention alone, then mla_post on the workspace's partials in its
-  request-major layout), and the request counters back at zero.
+  request-major layout), and every counter (the requests' and the unit
+  queue's) back at zero after each launch.
+The launch has two workgroups per CU, each taking units from a queue once
+its first is done; the cases with more (request, split) units than that
+(640 and 720 at 256 CUs, of ragged lengths) make workgroups take several.
 Inputs are seeded and synthetic (synth.decode_inputs).
 """
 
@@ -89,6 +93,9 @@ def check_case(m, d, **pads):
     # the unfused pair gives the same core, bit for bit
     ws2 = m.DecodeWorkspace(d.R, d.q, d.n)
     m.mla_decode(*args[:-1], ws2, fused=False)
+    torch.cuda.synchronize()
+    cnt = ws2.counters().cpu().numpy()
+    assert np.all(cnt == 0), f"counters not reset by the attention alone: {cnt[cnt != 0][:8]}"
     ov, lv, lay = ws2.token_views()
     core2 = m.mla_post(ov, lv, t["w_v"], t["w_s"], t["gate"], **lay)
     torch.cuda.synchronize()
@@ -114,6 +121,9 @@ CASES = [
     ("R_not_multiple_of_8", [40] * 13, 4, 3, 8, {}),
     ("strided", [90, 33, 160], 4, 3, 9, {"qry_pad": 64, "kv_pad": 32}),
     ("wide_scores", [120, 64], 4, 2, 10, {"q_sigma": 4.0}),
+    # more units than workgroups: each workgroup takes several from the queue
+    ("many_units", [int(x) for x in np.random.default_rng(11).integers(0, 150, 160)], 4, 4, 11, {}),
+    ("many_units_q1", [int(x) for x in np.random.default_rng(12).integers(1, 400, 90)], 1, 8, 12, {}),
 ]
 
 

@@ -29,6 +29,11 @@ SRCS = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
 NARROW_SAVE = re.compile(r"s_(and|andn2|or|xor)_saveexec_b64\s+(s\[\d+:\d+\]|vcc)")
 NARROW_OP = re.compile(r"s_(and|andn2|xor)_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\]|vcc)")
 RESTORE = re.compile(r"s_or_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\])")
+# an if/else: after the then-branch's saveexec into sY, s_xor sX, exec, sY
+# holds the else lanes; s_andn2_saveexec sX, sX switches exec to them (the
+# same depth), and s_or exec, exec, sX restores the exec of before the if
+ELSE_MASK = re.compile(r"s_xor_b64\s+(s\[\d+:\d+\]),\s*exec,\s*(s\[\d+:\d+\])")
+ELSE_SWITCH = re.compile(r"s_andn2_saveexec_b64\s+(s\[\d+:\d+\]),\s*(s\[\d+:\d+\])")
 
 
 def functions(asm: str) -> dict:
@@ -87,14 +92,23 @@ def basic_blocks(lines):
 def step(st: tuple, l: str) -> tuple:
     """The stack of exec narrowings after instruction l: a saveexec or an
     and/andn2/xor of exec pushes the register it uses; the s_or of exec with a
-    saved register pops back to that register's entry."""
+    saved register pops back to that register's entry. An entry holds the
+    registers that restore it ("sY|sX" once an if/else's else mask sX is
+    formed from sY); switching to the else branch keeps the depth."""
+    m = ELSE_MASK.match(l)
+    if m and st and m.group(2) in st[-1].split("|"):
+        return st[:-1] + (st[-1] + "|" + m.group(1),)
+    m = ELSE_SWITCH.match(l)
+    if m and st and m.group(1) == m.group(2) and m.group(1) in st[-1].split("|"):
+        return st
     m = NARROW_SAVE.match(l) or NARROW_OP.match(l)
     if m:
         return st + (m.group(2),)
     m = RESTORE.match(l)
-    if m and m.group(1) in st:
-        k = max(j for j, r in enumerate(st) if r == m.group(1))
-        return st[:k]
+    if m:
+        hits = [j for j, r in enumerate(st) if m.group(1) in r.split("|")]
+        if hits:
+            return st[:max(hits)]
     return st
 
 
