@@ -56,8 +56,9 @@ int mla_oproj_check(const void* core, int64_t core_stride, int32_t S, int32_t K,
                     int64_t w_stride, int32_t D, const void* out, int64_t out_stride);
 
 /* The launch mla_oproj makes for S x D on a device of `cus` compute units
- * (cus <= 0: the current device): *tile_m x *tile_n outputs per workgroup of
- * 256 threads, *workgroups in the grid. Host only. Returns a status code. */
+ * (cus <= 0: the current device): *tile_m x *tile_n outputs per workgroup (of
+ * 512 threads for 256 x 256 tiles, else 256), *workgroups in the grid. Host
+ * only. Returns a status code. */
 int mla_oproj_plan(int32_t S, int32_t D, int32_t cus, int32_t* tile_m, int32_t* tile_n, int32_t* workgroups);
 
 #ifdef __cplusplus

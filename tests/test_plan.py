@@ -308,13 +308,16 @@ def test_device_plan_is_the_table(gpu_lib):
 
 
 def test_oproj_plan_tiles():
-    """o_proj's tile at 256 CUs: 128 x 128 while that grid gives each CU two
-    workgroups (the large batch: 32 x 56 tiles), smaller tiles for small
-    batches; the grid covers S x D."""
+    """o_proj's tile at 256 CUs: 256 x 256 while that grid gives each CU a
+    workgroup (the large batch: 16 x 28 tiles), 128 x 128 while that grid
+    gives each CU two, smaller tiles for small batches; the grid covers S x
+    D."""
     import mla_split_kv_amd as m
 
     p = m.oproj_plan(4096, 7168, 256)
-    assert (p["tile_m"], p["tile_n"], p["workgroups"]) == (128, 128, 32 * 56)
+    assert (p["tile_m"], p["tile_n"], p["workgroups"]) == (256, 256, 16 * 28)
+    p = m.oproj_plan(2048, 7168, 256)  # 8 x 28 = 224 large tiles: fewer than the CUs
+    assert (p["tile_m"], p["tile_n"], p["workgroups"]) == (128, 128, 16 * 56)
     p = m.oproj_plan(64, 7168, 256)
     assert (p["tile_m"], p["tile_n"]) == (64, 64) and p["workgroups"] == 112
     for S, D in ((1, 8), (37, 136), (300, 1024), (4096, 7168), (5000, 264)):
