@@ -32,8 +32,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-KERNEL_SRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc", "mla_post.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_post_kernel.json")
+CSRC = os.path.join(ROOT, "mla_split_kv_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "mla_post.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hbm_per_launch.json")
+# Launches whose HBM traffic comes from committed counter runs: the entry's
+# name -> (a substring of the kernel's name in the counter CSVs, its source
+# file, what was measured).
+TRAFFIC_KERNELS = {
+    "large_decode": ("mla_post_kernel", "mla_post.hip", "mla_post_kernel<false, 1, 0> (large_decode workload)"),
+    "large_decode_request_major": (
+        "mla_post_kernel", "mla_post.hip", "mla_post_kernel<false, 1, 0> (large_decode_request_major workload)"),
+    "decode_attention": (
+        "mla_decode_kernel<false>", "decode.hip",
+        "mla_decode_kernel<false>: the attention alone, 1024 requests x 4 tokens, 16 splits, 4096 rows each"),
+    "decode_fused": (
+        "mla_decode_kernel<true>", "decode.hip",
+        "mla_decode_kernel<true>: attention and mla_post in one launch, same sizes"),
+    "oproj": ("oproj_big_kernel", "oproj.hip", "oproj_big_kernel: core [4096, 1536] x W_O [7168, 1536]^T"),
+}
 W_V_BYTES = 12 * 128 * 256 + 12 * 128 * 16  # MXFP4 codes + E8M0 scales, read once per launch
 
 
@@ -41,8 +57,8 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -263,12 +279,14 @@ def cpu_baseline_all_cores(w, tokens: int, workers: int) -> dict:
 
 def traffic_entry(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on this workload and on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    taken on this workload (a TRAFFIC_KERNELS entry) and on the current source
+    of its kernel."""
+    if not os.path.exists(TRAFFIC_FILE) or workload not in TRAFFIC_KERNELS:
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f).get(workload)
-    if not t or t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_sha():
+    src = os.path.join(CSRC, TRAFFIC_KERNELS[workload][1])
+    if not t or t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_sha(src):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -284,15 +302,16 @@ def counter_kib(csv_path: str, kernel_substr: str) -> list:
 
 def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
                  workload: str = "large_decode") -> dict:
-    """HBM bytes per launch of the fused kernel on `workload` from FETCH_SIZE /
-    WRITE_SIZE runs, each scaled by what the same counter reads for the plain
-    1 GiB copy (true bytes / counter bytes). Stored under the workload's name
-    in TRAFFIC_FILE (one entry per workload)."""
+    """HBM bytes per launch of a TRAFFIC_KERNELS entry's kernel from FETCH_SIZE
+    / WRITE_SIZE runs (median over its dispatches), each scaled by what the same
+    counter reads for the plain 1 GiB copy (true bytes / counter bytes).
+    Stored under the entry's name in TRAFFIC_FILE."""
     import statistics
 
+    sub, src, what = TRAFFIC_KERNELS[workload]
     copy_bytes = 1 << 30
-    fk = statistics.median(counter_kib(fetch_csv, "mla_post_kernel"))
-    wk = statistics.median(counter_kib(write_csv, "mla_post_kernel"))
+    fk = statistics.median(counter_kib(fetch_csv, sub))
+    wk = statistics.median(counter_kib(write_csv, sub))
     cf = statistics.median(counter_kib(copy_fetch_csv, "copyBuffer"))
     cw = statistics.median(counter_kib(copy_write_csv, "copyBuffer"))
     f_scale = copy_bytes / (cf * 1024)
@@ -300,9 +319,9 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write
     fetch = fk * 1024 * f_scale
     write = wk * 1024 * w_scale
     out = {
-        "kernel": f"mla_post_kernel<false, 1, 0> ({workload} workload)",
+        "kernel": what,
         "workload": workload,
-        "kernel_source_sha256": kernel_sha(),
+        "kernel_source_sha256": kernel_sha(os.path.join(CSRC, src)),
         "fetch_kib_per_dispatch": fk,
         "write_kib_per_dispatch": wk,
         "copy_fetch_kib": cf,
@@ -396,7 +415,8 @@ def oproj_bench(core, D: int, steps: int, warmup: int, m, torch) -> dict:
         "us_per_call": round(us, 3),
         "tflops": round(tflops, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_entry("oproj") if (S, D, K) == (4096, 7168, 1536) else None},
         "hbm_bytes_min": byts,
         "vendor_blas_us": round(us_blas, 3),
         "vs_vendor_blas": round(us_blas / us, 3),
@@ -457,6 +477,7 @@ def decode_bench(R: int, q: int, n: int, L: int, steps: int, warmup: int, m, tor
     torch.cuda.synchronize()
     same = bool(torch.equal(core, core2))
     alg = R * L * 1152 + S * 12 * 576 * 2 + W_V_BYTES + 2 * S * 1536 * 2
+    measured = (R, q, n, L) == (1024, 4, 16, 4096)  # the sizes of the committed counter runs
     gbps = alg / (res["fused"] * 1e-6) / 1e9
     out = {
         "workload": f"{R} requests x {q} tokens, {n} KV splits, {L} cache rows of 576 bf16 per request, 12 heads",
@@ -468,7 +489,9 @@ def decode_bench(R: int, q: int, n: int, L: int, steps: int, warmup: int, m, tor
         "tokens_per_s_fused": round(S / (res["fused"] * 1e-6), 1),
         "alg_bytes": alg,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_entry("decode_fused") if measured else None},
+        "attention_hbm_bytes": traffic_entry("decode_attention") if measured else None,
         "core_fused_equals_pair": same,
     }
     del qry, kv, ws
@@ -520,9 +543,12 @@ def main() -> int:
         metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
         help="turn rocprofv3 --pmc counter CSVs into the committed traffic figure (no GPU needed)",
     )
+    ap.add_argument("--traffic-entry", choices=sorted(TRAFFIC_KERNELS),
+                    help="with --traffic-from: the kernel and workload measured (default: --workload)")
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(traffic_from(*args.traffic_from, workload=args.workload), indent=1))
+        entry = args.traffic_entry or args.workload
+        print(json.dumps(traffic_from(*args.traffic_from, workload=entry), indent=1))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

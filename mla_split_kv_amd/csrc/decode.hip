@@ -514,7 +514,8 @@ __device__ __forceinline__ void decode_unit(const DArgs& a, int r, int j, uint8_
       // builtin's reads touch, so for it it waits for every load in flight
       // (the next blocks' too) first. Block b is complete and visible here
       // (the wait and barrier above), and the next barrier comes after this
-      // wave's reads have returned.
+      // wave's reads have returned. The outputs are early-clobber: the first
+      // read's result lands while later reads still use the address.
       const uint32_t vaddr = (uint32_t)(uintptr_t)(lds + (b % NBUF) * BLOCK_BYTES + (4 * g + (c16 >> 2)) * MROW +
                                                    (c16 & 3) * 8);
 #pragma unroll
@@ -530,7 +531,7 @@ __device__ __forceinline__ void decode_unit(const DArgs& a, int r, int j, uint8_
             "ds_read_b64_tr_b16 %6, %8 offset:%15\n"
             "ds_read_b64_tr_b16 %7, %8 offset:%16\n"
             "s_waitcnt lgkmcnt(0)"
-            : "=v"(lo0), "=v"(lo1), "=v"(lo2), "=v"(lo3), "=v"(hi0), "=v"(hi1), "=v"(hi2), "=v"(hi3)
+            : "=&v"(lo0), "=&v"(lo1), "=&v"(lo2), "=&v"(lo3), "=&v"(hi0), "=&v"(hi1), "=&v"(hi2), "=&v"(hi3)
             : "v"(vaddr), "i"(32 * c0), "i"(32 * c0 + 32), "i"(32 * c0 + 64), "i"(32 * c0 + 96),
               "i"(16 * MROW + 32 * c0), "i"(16 * MROW + 32 * c0 + 32), "i"(16 * MROW + 32 * c0 + 64),
               "i"(16 * MROW + 32 * c0 + 96));

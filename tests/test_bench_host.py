@@ -102,3 +102,28 @@ def test_cpu_baselines_report_fields():
     assert "first 8 of 128 tokens" in one["sample"]
     many = bench.cpu_baseline_all_cores(w, 16, 2)
     assert many["kind"] == "oracle" and many["cores"] == 2 and many["value"] > 0
+
+
+def test_traffic_entries_follow_their_own_source(tmp_path, monkeypatch):
+    """Each counter entry is valid only for the source file of its own kernel:
+    an edit of decode.hip voids the decode entries, not mla_post's or o_proj's."""
+    import shutil
+
+    csrc = tmp_path / "csrc"
+    shutil.copytree(bench.CSRC, csrc)
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(csrc / "mla_post.hip"))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    rows = "Kernel_Name,Counter_Value\n"
+    f = tmp_path / "f.csv"
+    f.write_text(rows + '"x::mla_decode_kernel<false>(a)",100\n"x::oproj_big_kernel(a)",10\n"copyBuffer",524288\n')
+    w = tmp_path / "w.csv"
+    w.write_text(rows + '"x::mla_decode_kernel<false>(a)",50\n"x::oproj_big_kernel(a)",5\n"copyBuffer",1048576\n')
+    d = bench.traffic_from(str(f), str(w), str(f), str(w), workload="decode_attention")
+    o = bench.traffic_from(str(f), str(w), str(f), str(w), workload="oproj")
+    assert d["hbm_bytes_per_launch"] == 100 * 2048 + 50 * 1024
+    assert o["hbm_bytes_per_launch"] == 10 * 2048 + 5 * 1024
+    assert bench.traffic_entry("decode_attention") == d["hbm_bytes_per_launch"]
+    (csrc / "decode.hip").write_text((csrc / "decode.hip").read_text() + "\n// edited\n")
+    assert bench.traffic_entry("decode_attention") is None
+    assert bench.traffic_entry("oproj") == o["hbm_bytes_per_launch"]

@@ -14,7 +14,8 @@ Each case checks:
   queue's) back at zero after each launch.
 The launch has two workgroups per CU, each taking units from a queue once
 its first is done; the cases with more (request, split) units than that
-(640 and 720 at 256 CUs, of ragged lengths) make workgroups take several.
+(640, 720, 2100 and 5500 at 256 CUs, of ragged lengths) make workgroups
+take several.
 Inputs are seeded and synthetic (synth.decode_inputs).
 """
 
@@ -124,6 +125,10 @@ CASES = [
     # more units than workgroups: each workgroup takes several from the queue
     ("many_units", [int(x) for x in np.random.default_rng(11).integers(0, 150, 160)], 4, 4, 11, {}),
     ("many_units_q1", [int(x) for x in np.random.default_rng(12).integers(1, 400, 90)], 1, 8, 12, {}),
+    # many requests with ragged lengths, some empty
+    ("ragged_300", [int(x) for x in np.random.default_rng(13).integers(0, 200, 300)], 4, 7, 13, {}),
+    # more requests than four per CU
+    ("requests_1100", [int(x) for x in np.random.default_rng(14).integers(0, 90, 1100)], 2, 5, 14, {}),
 ]
 
 
