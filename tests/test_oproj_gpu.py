@@ -50,6 +50,8 @@ def check(m, core_bits, w_bits, rows_per_chunk=1024):
         (4096, 7168, 1536),  # the large decode batch's core into a 7168-wide o_proj
         (4000, 7000, 1536),  # 256 x 256 tiles, ragged in both dimensions
         (2600, 6664, 960),  # 256 x 256 tiles, an odd number of K steps of 64
+        (4096, 4096, 1536),  # 256 x 256 tiles, one round on 256 CUs
+        (3900, 4000, 704),  # 256 x 256 tiles, ragged in both dimensions, 11 K steps of 64
         (1, 7168, 1536),
         (37, 7168, 1536),  # ragged token tile, small-batch tiling
         (300, 1024, 1536),  # between tilings
