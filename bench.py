@@ -349,7 +349,8 @@ def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16,
     o ~ N(0, 2), lse ~ N(8, 6) with 5% -inf, seed 4), generated once at the
     largest size; each size takes the first S tokens of it (strided views, as
     a caller would pass them). no_lse: one partial without LSEs instead (o ~
-    N(0, 1), seed 3)."""
+    N(0, 1), seed 3). Beside each: a plain streaming read of as many bytes
+    (mla_measure_read), and read_frac = its time over the call's."""
     import numpy as np
 
     import synth
@@ -366,6 +367,11 @@ def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16,
     d = device_setup(w, m, torch)
     lse_bytes = 0 if no_lse else splits * 12 * 4
     live_by_token = (np.full(smax, 12) if no_lse else np.isfinite(w.lse_view()).sum(axis=(0, 2)))
+    # the plain-read reference of each size: one streaming read of as many
+    # bytes as the call's algorithmic bytes, from a buffer of its own
+    alg_max = int(live_by_token.sum()) * 1024 + smax * lse_bytes + W_V_BYTES + 2 * smax * 1536 * 2
+    rbuf = torch.empty((alg_max + 15) // 16 * 16, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(16, dtype=torch.uint8, device="cuda")
     rows = []
     for S in sizes:
         lse = None if no_lse else d["lse"][:, :S]
@@ -374,9 +380,13 @@ def size_sweep(sizes: list, steps: int, warmup: int, m, torch, splits: int = 16,
         us = 1e3 * t["event_ms"] / steps
         alg = int(live_by_token[:S].sum()) * 1024 + S * lse_bytes + W_V_BYTES + 2 * S * 1536 * 2
         gbps = alg / (us * 1e-6) / 1e9
+        nread = (alg + 15) // 16 * 16
+        tr = time_gpu(lambda: m.measure_read(rbuf[:nread], sink), steps, warmup, torch)
+        read_us = 1e3 * tr["event_ms"] / steps
         rows.append({"S": S, "us_per_call": round(us, 3), "GBps": round(gbps, 1),
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "tokens_per_s": round(S / (us * 1e-6), 1),
-                     "alg_bytes": alg, "plan": m.plan(d["o"][:, :S], lse, d["w_v"], d["w_s"], d["gate"][:S])})
+                     "alg_bytes": alg, "read_us": round(read_us, 3), "read_frac": round(read_us / us, 4),
+                     "plan": m.plan(d["o"][:, :S], lse, d["w_v"], d["w_s"], d["gate"][:S])})
         log(f"S={S}: {rows[-1]}")
     what = "one partial without LSEs" if no_lse else f"{splits} splits, large decode distributions"
     return {"size_sweep": rows, "workload": f"{what}, first S tokens", "steps": steps}
