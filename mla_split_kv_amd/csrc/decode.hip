@@ -184,24 +184,48 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
     *reinterpret_cast<uint4*>(s_codes + h * LDS_CODES + b * CODE_ROW + slot * 16) = make_uint4(0u, 0u, 0u, 0u);
     s_scales[h * LDS_SCALES + slot * NBLK + b] = 1;
   }
-  // merge: wave w takes (token, head) rows p = w, w + 4, .. (np of them). Its
-  // LSE loads go out at once; the weights wait in LDS; then the partial rows
-  // of two (token, head) pairs at a time (32 rows in flight).
+  // merge: wave w takes (token, head) rows p = w, w + 4, .. (np of them), the
+  // partial rows of two (token, head) pairs at a time (32 rows in flight).
+  // The LSE loads go out first, then the first pair's rows, so the weights
+  // are computed while those rows are in flight; the weights wait in LDS.
   const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
       a.po + part_row(a, r, 0, 0, 0) * (KVL * 2), (short)0, a.n * qrows * KVL * 2, BUF_WORD3);
   const int np = (qrows - wave + DW - 1) / DW;  // wave-uniform, at most 12
   float* w_wave = s_w + wave * (MLA_DECODE_QMAX * NH / DW) * 64;
+  uint4 v[2][16];
+  // every row is loaded (an empty split's partial is +0, written by its
+  // unit), then added with its weight: a weight of 0 adds +0, which leaves
+  // the sum's bits as skipping the row would (the sum starts at +0 and never
+  // becomes -0). The rows are read once: non-temporal (measured: the fused
+  // launch 1207 -> 1188 us on the large decode batch)
+  auto load_rows = [&](int i0, int j0) {
+    const int p0 = wave + DW * i0, p1 = wave + DW * min(i0 + 1, np - 1);
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int j = min(j0 + b, a.n - 1);
+      const v4u x0 = (v4u)__builtin_amdgcn_raw_buffer_load_b128(
+          rres, (int)(part_row(a, 0, j, p0 / NH, p0 % NH) * (KVL * 2)) + lane * 16, 0, CPOL_AGENT | CPOL_NT);
+      const v4u x1 = (v4u)__builtin_amdgcn_raw_buffer_load_b128(
+          rres, (int)(part_row(a, 0, j, p1 / NH, p1 % NH) * (KVL * 2)) + lane * 16, 0, CPOL_AGENT | CPOL_NT);
+      v[0][b] = make_uint4(x0.x, x0.y, x0.z, x0.w);
+      v[1][b] = make_uint4(x1.x, x1.y, x1.z, x1.w);
+    }
+  };
   {
+    // every lane loads (split min(lane, n - 1) of pair min(i, np - 1)) and
+    // takes -inf where the split or the pair does not exist: no branch
+    // around the loads
     float l[MLA_DECODE_QMAX * NH / DW];
 #pragma unroll
     for (int i = 0; i < MLA_DECODE_QMAX * NH / DW; ++i) {
-      const int p = wave + DW * i;
-      l[i] = -INFINITY;
-      if (i < np && lane < a.n)
-        l[i] = __hip_atomic_load(a.pl + part_row(a, r, lane, p / NH, p % NH), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int p = wave + DW * min(i, np - 1);
+      l[i] = __hip_atomic_load(a.pl + part_row(a, r, min(lane, a.n - 1), p / NH, p % NH), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
+    load_rows(0, 0);
 #pragma unroll
-    for (int i = 0; i < MLA_DECODE_QMAX * NH / DW; ++i) w_wave[i * 64 + lane] = sane(l[i]);
+    for (int i = 0; i < MLA_DECODE_QMAX * NH / DW; ++i)
+      w_wave[i * 64 + lane] = (i < np && lane < a.n) ? sane(l[i]) : -INFINITY;
   }
 #pragma unroll 1
   for (int i = 0; i < np; ++i) {
@@ -216,26 +240,9 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[e][k] = 0.f;
-    const int p0 = wave + DW * i0, p1 = wave + DW * min(i0 + 1, np - 1);
 #pragma unroll 1
     for (int j0 = 0; j0 < a.n; j0 += 16) {
-      // every row is loaded (an empty split's partial is +0, written by its
-      // unit), then added with its weight: a weight of 0 adds +0, which
-      // leaves the sum's bits as skipping the row would (the sum starts at
-      // +0 and never becomes -0). The rows are read once: non-temporal
-      // (measured: the fused launch 1207 -> 1188 us on the large decode
-      // batch)
-      uint4 v[2][16];
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const int j = min(j0 + b, a.n - 1);
-        const v4u x0 = (v4u)__builtin_amdgcn_raw_buffer_load_b128(
-            rres, (int)(part_row(a, 0, j, p0 / NH, p0 % NH) * (KVL * 2)) + lane * 16, 0, CPOL_AGENT | CPOL_NT);
-        const v4u x1 = (v4u)__builtin_amdgcn_raw_buffer_load_b128(
-            rres, (int)(part_row(a, 0, j, p1 / NH, p1 % NH) * (KVL * 2)) + lane * 16, 0, CPOL_AGENT | CPOL_NT);
-        v[0][b] = make_uint4(x0.x, x0.y, x0.z, x0.w);
-        v[1][b] = make_uint4(x1.x, x1.y, x1.z, x1.w);
-      }
+      if (i0 | j0) load_rows(i0, j0);  // the first pair's rows are in flight already
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
         const int j = j0 + b;
@@ -245,6 +252,7 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
         fma_row(wb, v[1][b], acc[1]);
       }
     }
+    const int p0 = wave + DW * i0, p1 = wave + DW * min(i0 + 1, np - 1);
 #pragma unroll 1
     for (int e = 0; e < 2 && i0 + e < np; ++e) {
       const int p = e ? p1 : p0;
@@ -264,32 +272,41 @@ __device__ void consume(const DArgs& a, int r, uint8_t* lds) {
       if (a.dbg_scales && (lane & 3) == 0) a.dbg_scales[th * NBLK + b] = (uint8_t)code;
     }
   }
-  __syncthreads();
-  // W_UV: wave w takes heads w, w + 4, w + 8; per head 8 tiles of 16 W_V rows
+  // W_UV: wave w takes heads w, w + 4, w + 8; per head 8 tiles of 16 W_V
+  // rows. The head's W_V operands for all 8 row tiles come in one round
+  // trip; the first head's are requested before the barrier that ends the
+  // merge (which waits for LDS only), so they are in flight while the other
+  // waves finish it.
   const int tl = lane & 15, kb = lane >> 4;
   const int tok = min(tl, a.q - 1);  // gate row of this lane's column (columns past q are never stored)
-#pragma unroll 1
-  for (int h = wave; h < NH; h += DW) {
-    const int sb = *reinterpret_cast<const int*>(s_scales + h * LDS_SCALES + tl * NBLK + kb * 4);
-    const uint8_t* brow = s_codes + h * LDS_CODES + tl * 16;
-    // the head's W_V operands for all 8 row tiles, and their gate values, in
-    // one round trip
-    uint4 wv[VD / 16][4];
-    int sa[VD / 16];
-    uint2 g4[VD / 16];
+  uint4 wv[VD / 16][4];
+  int sa[VD / 16];
+  auto load_head = [&](int h) {
 #pragma unroll
     for (int rt = 0; rt < VD / 16; ++rt) {
-      const int v = rt * 16 + tl;
-      const uint8_t* wrow = a.w_v + h * a.w_sh + v * a.w_sv + kb * 16;
-      const uint8_t* srow = a.w_vs + h * a.s_sh + v * a.s_sv;
+      const int vrow = rt * 16 + tl;
+      const uint8_t* wrow = a.w_v + h * a.w_sh + vrow * a.w_sv + kb * 16;
+      const uint8_t* srow = a.w_vs + h * a.s_sh + vrow * a.s_sv;
       sa[rt] = 0;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         wv[rt][st] = *reinterpret_cast<const uint4*>(wrow + st * 64);
         sa[rt] |= (int)srow[(st * 4 + kb) * a.s_sb] << (8 * st);
       }
-      g4[rt] = *reinterpret_cast<const uint2*>(a.gate + ((int64_t)(r * a.q + tok) * GROWS + h * VD + rt * 16 + kb * 4) * 2);
     }
+  };
+  load_head(wave);
+  lds_barrier();
+#pragma unroll 1
+  for (int h = wave; h < NH; h += DW) {
+    if (h != wave) load_head(h);
+    // the gate values, used after the MFMAs
+    uint2 g4[VD / 16];
+#pragma unroll
+    for (int rt = 0; rt < VD / 16; ++rt)
+      g4[rt] = *reinterpret_cast<const uint2*>(a.gate + ((int64_t)(r * a.q + tok) * GROWS + h * VD + rt * 16 + kb * 4) * 2);
+    const int sb = *reinterpret_cast<const int*>(s_scales + h * LDS_SCALES + tl * NBLK + kb * 4);
+    const uint8_t* brow = s_codes + h * LDS_CODES + tl * 16;
 #pragma unroll
     for (int rt = 0; rt < VD / 16; ++rt) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
