@@ -161,3 +161,43 @@ def test_decode_empty_batch_and_errors(gpu_lib):
         m.DecodeWorkspace(1, 5, 2)
     with pytest.raises(m.MlaPostError):  # n past MLA_DECODE_NMAX
         m.DecodeWorkspace(1, 4, 65)
+
+
+# Seeded random configurations: request counts on both sides of one unit
+# per CU pair (512 at 256 CUs), one to four tokens, 1 to 64 splits, ragged
+# lengths with empty requests and splits shorter than a block, strided
+# queries and cache rows, wide score spreads. Each case runs the whole
+# check_case (T0 on the partials, T1-T4 on every token, fused == unfused bit
+# for bit, counters back at zero) and is named before it runs.
+RANDOM_CASES = 16
+MAX_KV_ROWS = 50_000  # total cache rows of a case: the oracle's attention stays in seconds
+
+
+def random_case(i):
+    rng = np.random.default_rng(7000 + i)
+    R = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(40, 512)), int(rng.integers(512, 900))]))
+    q = int(rng.integers(1, 5))
+    n = int(rng.choice([1, 2, 3, int(rng.integers(4, 17)), int(rng.integers(17, 65))]))
+    mean = max(1, MAX_KV_ROWS // R)
+    lens = rng.integers(0, 2 * mean + 1, R)
+    lens[rng.random(R) < 0.1] = 0
+    short = rng.random(R) < 0.1
+    lens[short] = rng.integers(1, n + 1, int(short.sum()))  # splits of 0 or 1 rows
+    opts = {}
+    if rng.random() < 0.3:
+        opts["q_sigma"] = float(rng.choice([3.0, 6.0]))
+    pads = {}
+    if rng.random() < 0.3:
+        pads = {"qry_pad": int(rng.choice([8, 64])), "kv_pad": int(rng.choice([8, 32]))}
+    return f"rand{i}", [int(x) for x in lens], q, n, 8000 + i, opts, pads
+
+
+@pytest.mark.parametrize("i", range(RANDOM_CASES))
+def test_decode_random(gpu_lib, i):
+    name, lens, q, n, seed, opts, pads = random_case(i)
+    say(f"random decode case {i}: R={len(lens)} q={q} n={n} rows={sum(lens)} opts={opts} pads={pads}")
+    d = synth.decode_inputs(name, lens, q, n, seed, **opts)
+    st, g, _ = check_case(gpu_lib, d, **pads)
+    lens = np.asarray(lens)
+    for r in np.nonzero(lens == 0)[0]:
+        assert np.all(g["core"][r * q : (r + 1) * q] == 0)
