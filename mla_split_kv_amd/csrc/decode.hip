@@ -588,7 +588,11 @@ __device__ __forceinline__ void decode_unit(const DArgs& a, int r, int j, uint8_
   // zeros and -inf). Each compute wave stages its 16 rows in LDS (the KV
   // blocks are free after the barrier above) and writes each row's 1 KiB as
   // one store of 16 bytes per lane: whole cache lines, since the partials are
-  // written through to the device's coherence point (sc1).
+  // written through to the device's coherence point (sc1). The attention
+  // alone also stores them non-temporal: they are read by another launch,
+  // long after, so keeping them in the caches only pushes out the queries
+  // (measured on the large decode batch: 1030 -> 1005 us; in the fused launch
+  // the merge reads them soon after, and non-temporal stores were slower).
   uint8_t* ot = lds + wave * 16 * MROW;  // this wave's rows, MROW bytes apart
   const bool any = nblk > 0;
   if (compute) {
@@ -608,7 +612,8 @@ __device__ __forceinline__ void decode_unit(const DArgs& a, int r, int j, uint8_
       const uint4 v = *reinterpret_cast<const uint4*>(ot + i * MROW + lane * 16);
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(a.po + row * (KVL * 2), (short)0, KVL * 2, BUF_WORD3);
-      __builtin_amdgcn_raw_buffer_store_b128((v4u){v.x, v.y, v.z, v.w}, rs, lane * 16, 0, CPOL_AGENT);
+      __builtin_amdgcn_raw_buffer_store_b128((v4u){v.x, v.y, v.z, v.w}, rs, lane * 16, 0,
+                                             FUSED ? CPOL_AGENT : CPOL_AGENT | CPOL_NT);
     }
     if (g == 0 && qi < qrows)
       __hip_atomic_store(a.pl + part_row(a, r, j, qi / NH, qi % NH), lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -34,6 +34,10 @@ RESTORE = re.compile(r"s_or_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\])")
 # same depth), and s_or exec, exec, sX restores the exec of before the if
 ELSE_MASK = re.compile(r"s_xor_b64\s+(s\[\d+:\d+\]),\s*exec,\s*(s\[\d+:\d+\])")
 ELSE_SWITCH = re.compile(r"s_andn2_saveexec_b64\s+(s\[\d+:\d+\]),\s*(s\[\d+:\d+\])")
+# the same narrowing written out: s_mov sX, exec saves exec, s_and sY, sX, cond
+# forms the mask, s_mov exec, sY narrows, s_or exec, exec, sX restores
+SAVE_MOV = re.compile(r"s_mov_b64\s+(s\[\d+:\d+\]),\s*exec\b")
+SET_MOV = re.compile(r"s_mov_b64\s+exec,\s*(s\[\d+:\d+\])")
 
 
 def functions(asm: str) -> dict:
@@ -89,12 +93,29 @@ def basic_blocks(lines):
     return bl
 
 
+def depth(st: tuple) -> int:
+    """Exec narrowings in force (entries starting with "=" only record the
+    latest copy of exec, see step)."""
+    return sum(1 for e in st if not e.startswith("="))
+
+
 def step(st: tuple, l: str) -> tuple:
     """The stack of exec narrowings after instruction l: a saveexec or an
     and/andn2/xor of exec pushes the register it uses; the s_or of exec with a
     saved register pops back to that register's entry. An entry holds the
     registers that restore it ("sY|sX" once an if/else's else mask sX is
-    formed from sY); switching to the else branch keeps the depth."""
+    formed from sY); switching to the else branch keeps the depth. The
+    written-out form: s_mov sX, exec records "=sX"; s_mov exec, sY then
+    pushes sX (or "?" with no copy recorded, which the next s_or of exec with
+    a register not on the stack pops)."""
+    m = SAVE_MOV.match(l)
+    if m:
+        return tuple(e for e in st if not e.startswith("=")) + ("=" + m.group(1),)
+    m = SET_MOV.match(l)
+    if m:
+        saved = [e[1:] for e in st if e.startswith("=")]
+        rest = tuple(e for e in st if not e.startswith("="))
+        return rest + ((saved[-1] if saved else "?"),)
     m = ELSE_MASK.match(l)
     if m and st and m.group(2) in st[-1].split("|"):
         return st[:-1] + (st[-1] + "|" + m.group(1),)
@@ -107,6 +128,8 @@ def step(st: tuple, l: str) -> tuple:
     m = RESTORE.match(l)
     if m:
         hits = [j for j, r in enumerate(st) if m.group(1) in r.split("|")]
+        if not hits:
+            hits = [j for j, r in enumerate(st) if r == "?"]
         if hits:
             return st[:max(hits)]
     return st
@@ -128,7 +151,7 @@ def exec_depths(asm: str):
                 st = step(st, l)
             for s in bl[i]["succ"]:
                 old = state.get(s)
-                if old is None or (len(st) > len(old) and len(st) <= 16):
+                if old is None or (depth(st) > depth(old) and depth(st) <= 16):
                     state[s] = st
                     work.append(s)
         for i, b in enumerate(bl):
@@ -136,7 +159,7 @@ def exec_depths(asm: str):
             for l in b["ins"]:
                 st = step(st, l)
                 if l.startswith("v_mfma") or re.match(r"(global|buffer)_store", l):
-                    out.append((fn, l.split()[0], len(st)))
+                    out.append((fn, l.split()[0], depth(st)))
     return out
 
 
@@ -162,3 +185,36 @@ def test_mfma_under_full_exec(tmp_path, src):
     assert not masked, f"MFMAs under a narrowed exec mask: {masked[:5]}"
     # the same scan sees the lane-conditional stores, so it does see narrowing
     assert any(d > 0 for _, m, d in rows if "store" in m), "the scan found no narrowed region at all"
+
+
+def _fake_kernel(body: str) -> str:
+    return "_Z4fakev:\n" + "\n".join("\t" + l.strip() for l in body.strip().splitlines()) + "\n.Lfunc_end0:\n"
+
+
+@pytest.mark.parametrize("form", ["saveexec", "written_out"])
+def test_scan_sees_both_narrowing_forms(form):
+    """The scan on hand-made code: an MFMA inside a lane-dependent loop is
+    found narrowed in either form the compiler writes the narrowing, and
+    MFMAs before it and after the restore are not."""
+    if form == "saveexec":
+        enter = "s_and_saveexec_b64 s[4:5], vcc"
+    else:
+        enter = "s_mov_b64 s[4:5], exec\ns_and_b64 s[6:7], s[4:5], vcc\ns_mov_b64 exec, s[6:7]"
+    asm = _fake_kernel(f"""
+        v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], v[0:3]
+        {enter}
+        s_cbranch_execz .LBB0_3
+        s_mov_b64 s[8:9], 0
+        .LBB0_2:
+        v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], v[0:3]
+        global_store_dwordx4 v[12:13], v[0:3], off
+        s_or_b64 s[8:9], vcc, s[8:9]
+        s_andn2_b64 exec, exec, s[8:9]
+        s_cbranch_execnz .LBB0_2
+        .LBB0_3:
+        s_or_b64 exec, exec, s[4:5]
+        v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], v[0:3]
+        s_endpgm
+    """)
+    d = [x[2] for x in exec_depths(asm) if x[1].startswith("v_mfma")]
+    assert d[0] == 0 and d[1] > 0 and d[2] == 0, d
