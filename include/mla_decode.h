@@ -79,7 +79,9 @@ typedef struct mla_decode_args {
 
   void* workspace;         /* device memory of mla_decode_workspace's size, 256-byte aligned; its
                               counters must be zero before the first call (mla_decode_workspace_init)
-                              and are zero again after every call */
+                              and are zero again after every call. Counters that are not zero give
+                              wrong or missing results, never an access outside the arguments'
+                              buffers: a queue value outside the batch names no unit */
   int64_t workspace_bytes;
 
   /* optional stage outputs of the merge (NULL to skip), as mla_post's:

@@ -671,7 +671,11 @@ __global__ __launch_bounds__(DTHREADS, 2) void mla_decode_kernel(const DArgs a) 
     // every wave is done with the unit's LDS before any starts the next (the
     // attention's partial stores stay in flight)
     lds_barrier();
-    u = (int)gridDim.x + __builtin_amdgcn_readfirstlane(*s_next);
+    // a claim past the batch ends the loop; so does any value a counter
+    // that was not zero at the launch can give, so no unit outside the
+    // batch is ever named
+    const int c = __builtin_amdgcn_readfirstlane(*s_next);
+    u = c >= 0 && c < units - (int)gridDim.x ? (int)gridDim.x + c : units;
   }
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(q_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
