@@ -158,6 +158,9 @@ _lib = None
 
 
 class MlaPostError(RuntimeError):
+    """A non-zero MLA_POST_* status from the library: `status` is the code,
+    the message its name and the library's detail."""
+
     def __init__(self, status: int, detail: str = ""):
         self.status = status
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -380,6 +383,8 @@ class Prepared:
 
 
 def prepare(o, lse, w_v, w_v_scale, gate, core, **layout):
+    """A validated mla_post call on these tensors, to be launched again and
+    again (`Prepared`): the arguments are checked and marshalled once."""
     return Prepared(o, lse, w_v, w_v_scale, gate, core, **layout)
 
 
