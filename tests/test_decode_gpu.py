@@ -15,7 +15,9 @@ Each case checks:
 The launch has two workgroups per CU, each taking units from a queue once
 its first is done; the cases with more (request, split) units than that
 (640, 720, 2100 and 5500 at 256 CUs, of ragged lengths) make workgroups
-take several.
+take several. The bench's full size (1024 requests x 4 tokens, 16 splits,
+4096 rows each) is checked on eight sampled requests against the oracles
+and on the whole core against the unfused pair.
 Inputs are seeded and synthetic (synth.decode_inputs).
 """
 
@@ -201,3 +203,62 @@ def test_decode_random(gpu_lib, i):
     lens = np.asarray(lens)
     for r in np.nonzero(lens == 0)[0]:
         assert np.all(g["core"][r * q : (r + 1) * q] == 0)
+
+
+FULL_R, FULL_Q, FULL_N, FULL_L = 1024, 4, 16, 4096
+
+
+def test_decode_full_size_sampled(gpu_lib):
+    """The bench's decode workload at full size: 1024 requests of 4 tokens, 16
+    splits, 4096 cache rows of 576 bf16 each (4.83 GB of KV), in the launch
+    the bench times (two persistent workgroups per CU). The oracles check
+    eight requests (both ends, around the middle, three seeded picks): their
+    partials against the attention oracle (T0), their tokens' merge stage and
+    core against the mla_post oracle (T1-T4). The whole core is checked bit
+    for bit against the unfused pair and against the same launch without
+    stage outputs, and every counter is back at zero."""
+    m = gpu_lib
+    R, q, n, L = FULL_R, FULL_Q, FULL_N, FULL_L
+    say(f"full size: R={R} q={q} n={n} L={L}: drawing the inputs")
+    d = synth.decode_inputs("decode_full_size", [L] * R, q, n, 9001)
+    t = device_case(d)
+    ws = m.DecodeWorkspace(R, q, n)
+    args = (t["qry"], t["kv"], t["indptr"], q, n, d.scale, t["w_v"], t["w_s"], t["gate"], ws)
+    say("full size: fused launch with stage outputs")
+    core, lat, codes, scales = m.mla_decode(*args, debug=True)
+    torch.cuda.synchronize()
+    cnt = ws.counters().cpu().numpy()
+    assert np.all(cnt == 0), f"counters not reset: {cnt[cnt != 0][:8]}"
+    core_h = to_bits(core)
+    po, pl = ws.partials()
+    rng = np.random.default_rng(9002)
+    pick = sorted({0, 1, R // 2 - 1, R // 2, R - 1} | {int(x) for x in rng.integers(0, R, 3)})
+    nrows = np.diff(A.split_bounds(L, n))[None]
+    for r in pick:
+        toks = slice(r * q, (r + 1) * q)
+        po_h, pl_h = to_bits(po[r : r + 1]), pl[r : r + 1].cpu().numpy()
+        ref = A.attention_partials(d.qry[toks], d.kv[r * L : (r + 1) * L], np.array([0, L], np.int32), q, n, d.scale)
+        st = C.check_t0(po_h, pl_h, ref, nrows)
+        o_tok = np.ascontiguousarray(np.transpose(po_h, (1, 0, 2, 3, 4)).reshape(n, q, 12, 512))
+        l_tok = np.ascontiguousarray(np.transpose(pl_h, (1, 0, 2, 3)).reshape(n, q, 12))
+        g = {"core": core_h[toks], "lat": to_bits(lat[toks]), "codes": codes[toks].cpu().numpy(),
+             "scales": scales[toks].cpu().numpy()}
+        st.update(C.check_all(o_tok, l_tok, t["wc"], t["ws"], d.gate[toks], g))
+        say(f"full size: request {r}: {st}")
+    # the launch the bench times (no stage outputs): the same core
+    core_b = m.mla_decode(*args)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(core_b), core_h), "the launch without stage outputs gives another core"
+    del lat, codes, scales, core_b
+    # the unfused pair: the same core, bit for bit
+    ws2 = m.DecodeWorkspace(R, q, n)
+    m.mla_decode(*args[:-1], ws2, fused=False)
+    ov, lv, lay = ws2.token_views()
+    core2 = m.mla_post(ov, lv, t["w_v"], t["w_s"], t["gate"], **lay)
+    torch.cuda.synchronize()
+    cnt = ws2.counters().cpu().numpy()
+    assert np.all(cnt == 0), f"counters not reset by the attention alone: {cnt[cnt != 0][:8]}"
+    assert np.array_equal(to_bits(core2), core_h), "fused and unfused core differ"
+    say(f"full size: {len(pick)} requests checked against the oracles, core equal to the unfused pair")
+    del ws, ws2, core, core2, po, pl, ov, lv, t
+    torch.cuda.empty_cache()
